@@ -1,0 +1,181 @@
+/*
+ * moe_int8.h -- C ABI of libmoe_int8.so: the forward pass of a mixture-of-experts
+ * feed-forward layer whose expert weights are stored as int8 (MI355X / gfx950).
+ *
+ * What the layer computes (Jamba-1.5 paper, "Model Architecture"): an MoE module
+ * stands in for the MLP; a router scores n experts per token and the top K are
+ * used (n=16, K=2 in Jamba). "Serving Considerations and Improvements" (the
+ * ExpertsInt8 scheme): expert weights live in memory as INT8, are turned back
+ * into BF16 values inside the fused MoE kernel, and activations stay BF16.
+ *
+ * Readings of what the paper leaves open, implemented by every call below:
+ *   gate    p = softmax(l) over all E logits l = x . router_w[e] (+ bias[e]);
+ *           the K largest logits, descending, exact ties to the lower index;
+ *           w_k = p_k / sum of p over the K chosen experts.
+ *   expert  SwiGLU: o = s_d * (q_d . h), h = silu(g) * u,
+ *           g = s_g * (q_g . x), u = s_u * (q_u . x); no biases.
+ *   int8    symmetric, one scale per output channel (row of an (out, in)
+ *           matrix); moe_quantize_rows below produces the codes and scales.
+ *   combine y_t = sum_k w_k * o_{t,k}; no capacity limit, no residual.
+ * The contractions run on bf16 MFMA with fp32 accumulation: int8 codes become
+ * bf16 exactly, activations given as fp32 are rounded to bf16 at the MFMA input,
+ * the per-channel scale is applied to the fp32 sum, h is held as bf16, the
+ * per-slot expert outputs (y_rows) as fp32.
+ *
+ * Conventions (all calls):
+ *   - Pointers named x, router_w, y, w_*, s_*, topk_*, expert_offsets,
+ *     sorted_slots, slot_to_row, y_rows and workspace are DEVICE pointers on
+ *     the current HIP device, row-major, 16-byte aligned. The caller owns
+ *     every buffer; the library allocates nothing and keeps no state between
+ *     calls, so calls on different streams may run concurrently.
+ *   - Work is enqueued on `stream` and is asynchronous; no call synchronises.
+ *   - Arguments are validated before anything is enqueued. On error nothing is
+ *     launched and a moe_status other than MOE_OK is returned; the message is
+ *     available from moe_last_error() on the calling thread. A launch failure
+ *     reported by HIP maps to MOE_ERR_HIP. Device-side faults surface at the
+ *     caller's next synchronisation.
+ *   - Weight layout is (out, in): w_gate, w_up [E, f, d]; w_down [E, d, f];
+ *     router_w [E, d]; scales s_gate, s_up [E, f], s_down [E, d].
+ *   - Slots: token t's k-th choice is slot s = t*K + k.
+ *   - T = 0 is valid and enqueues nothing.
+ */
+#ifndef MOE_INT8_H
+#define MOE_INT8_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t moe_status;
+enum {
+  MOE_OK = 0,
+  MOE_ERR_NULL = 1,        /* a required pointer is NULL */
+  MOE_ERR_SHAPE = 2,       /* a size is out of range or not a supported multiple */
+  MOE_ERR_DTYPE = 3,       /* unknown dtype code */
+  MOE_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned */
+  MOE_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required */
+  MOE_ERR_UNSUPPORTED = 6, /* valid request this build does not implement */
+  MOE_ERR_HIP = 7          /* a HIP runtime call failed */
+};
+
+/* dtype codes */
+enum { MOE_F32 = 0, MOE_BF16 = 1 };
+
+/* expert-FFN schedule: AUTO picks STREAM when few rows fall on each expert
+ * (decode) and TILED otherwise (prefill). Both give results within the same
+ * tolerance of the exact layer; they are not bit-identical to each other. */
+enum { MOE_PATH_AUTO = 0, MOE_PATH_STREAM = 1, MOE_PATH_TILED = 2 };
+
+typedef struct moe_shape {
+  int32_t T;           /* tokens, >= 0                                     */
+  int32_t d;           /* hidden size, multiple of 64, 64..65536            */
+  int32_t f;           /* expert FFN width, multiple of 64, 64..131072      */
+  int32_t E;           /* experts, 1..64                                    */
+  int32_t K;           /* experts per token, 1..min(E, 8)                   */
+  int32_t act_dtype;   /* x, router_w, y: MOE_F32 or MOE_BF16               */
+  int32_t scale_dtype; /* s_gate, s_up, s_down: MOE_F32 or MOE_BF16         */
+  int32_t ffn_path;    /* MOE_PATH_*                                        */
+} moe_shape;
+
+/* ABI version of this header (bumped on any signature change). */
+#define MOE_ABI_VERSION 1
+int32_t moe_abi_version(void);
+
+/* Static description of a status code. */
+const char* moe_status_str(moe_status status);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* moe_last_error(void);
+
+/* Workspace, in bytes, that moe_forward needs for this shape (includes the
+ * routing buffers, the permutation, h and y_rows). */
+moe_status moe_workspace_size(const moe_shape* shape, size_t* bytes);
+
+/* Workspace, in bytes, that moe_expert_ffn needs (h: T*K*f bf16, plus padding). */
+moe_status moe_ffn_workspace_size(const moe_shape* shape, size_t* bytes);
+
+/* Router and gate (paper: "Model Architecture", top K of n experts per token).
+ *   x           [T, d]  act_dtype
+ *   router_w    [E, d]  act_dtype
+ *   router_bias [E] fp32 added to the logits, or NULL
+ *   topk_ids    [T, K] int32 out: chosen experts, descending logit
+ *   topk_w      [T, K] fp32  out: renormalised gate weights (sum to 1 per token)
+ * Logits are fp32 dot products of the exact inputs. */
+moe_status moe_route(const moe_shape* shape, const void* x, const void* router_w,
+                     const float* router_bias, int32_t* topk_ids, float* topk_w,
+                     hipStream_t stream);
+
+/* Group the T*K slots by expert (stable: ascending slot inside an expert).
+ *   topk_ids       [T*K] int32 in, values in [0, E)
+ *   expert_offsets [E+1] int32 out: expert e owns sorted rows [off[e], off[e+1])
+ *   sorted_slots   [T*K] int32 out: slot held by each sorted row
+ *   slot_to_row    [T*K] int32 out: sorted row of each slot
+ * An id outside [0, E) is not placed: its slot_to_row entry is -1 and the
+ * sorted rows past off[E] hold -1. Bit-exact and deterministic. */
+moe_status moe_permute(const moe_shape* shape, const int32_t* topk_ids,
+                       int32_t* expert_offsets, int32_t* sorted_slots,
+                       int32_t* slot_to_row, hipStream_t stream);
+
+/* Expert SwiGLU FFNs on the permuted rows (the ExpertsInt8 contraction).
+ *   x              [T, d] act_dtype (row of sorted row r is token sorted_slots[r] / K)
+ *   expert_offsets [E+1], sorted_slots [T*K] from moe_permute
+ *   w_gate, w_up   [E, f, d] int8;  w_down [E, d, f] int8
+ *   s_gate, s_up   [E, f] scale_dtype;  s_down [E, d] scale_dtype
+ *   y_rows         [T*K, d] fp32 out: row r = output of sorted row r's expert
+ *   workspace      >= moe_ffn_workspace_size bytes (holds h)
+ * Rows past off[E] are left untouched. */
+moe_status moe_expert_ffn(const moe_shape* shape, const void* x,
+                          const int32_t* expert_offsets, const int32_t* sorted_slots,
+                          const int8_t* w_gate, const int8_t* w_up, const int8_t* w_down,
+                          const void* s_gate, const void* s_up, const void* s_down,
+                          float* y_rows, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream);
+
+/* The two passes of moe_expert_ffn, callable on their own (same kernels):
+ * gate/up  h[r] = silu(s_g * (q_g . x_r)) * (s_u * (q_u . x_r))  for every sorted row r,
+ *          h [T*K, f] bf16 out (rows past off[E] untouched);
+ * down     y_rows[r] = s_d * (q_d . h[r]),  h [T*K, f] bf16 in, y_rows [T*K, d] fp32 out.
+ * moe_expert_ffn is moe_expert_gate_up followed by moe_expert_down on the same stream. */
+moe_status moe_expert_gate_up(const moe_shape* shape, const void* x, const int32_t* expert_offsets,
+                              const int32_t* sorted_slots, const int8_t* w_gate, const int8_t* w_up,
+                              const void* s_gate, const void* s_up, void* h, hipStream_t stream);
+moe_status moe_expert_down(const moe_shape* shape, const void* h, const int32_t* expert_offsets,
+                           const int8_t* w_down, const void* s_down, float* y_rows, hipStream_t stream);
+
+/* Weighted combine back to token order: y[t] = sum_k topk_w[t,k] * y_rows[slot_to_row[t*K+k]]
+ * (k ascending, fp32, no atomics); a slot with row -1 contributes nothing.
+ *   y [T, d] act_dtype out. */
+moe_status moe_combine(const moe_shape* shape, const float* y_rows, const int32_t* slot_to_row,
+                       const float* topk_w, void* y, hipStream_t stream);
+
+/* The whole layer: route, permute, expert FFN, combine, enqueued on `stream`.
+ * Bit-identical to the four staged calls above with the same ffn_path.
+ *   topk_ids_out [T, K] / topk_w_out [T, K]: optional copies of the routing (NULL to skip)
+ *   workspace    >= moe_workspace_size bytes */
+moe_status moe_forward(const moe_shape* shape, const void* x, const void* router_w,
+                       const float* router_bias,
+                       const int8_t* w_gate, const int8_t* w_up, const int8_t* w_down,
+                       const void* s_gate, const void* s_up, const void* s_down,
+                       void* y, int32_t* topk_ids_out, float* topk_w_out,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ExpertsInt8 quantizer (paper: "Serving Considerations and Improvements":
+ * quantized at load time in seconds, no calibration). Row-wise symmetric int8:
+ *   a = max_i |w[r, i]|,  s[r] = a / 127 rounded once (nearest-even) to scale_dtype,
+ *   q[r, i] = round-half-even(w[r, i] / s[r]) clamped to [-127, 127];
+ *   an all-zero row gives s = 0 and q = 0.
+ *   w [rows, cols] src_dtype (MOE_F32 or MOE_BF16), q [rows, cols] int8, s [rows].
+ * Quantizing an (out, in) weight [E, out, in] is rows = E*out, cols = in.
+ * cols must be a multiple of 16, 16..1048576. Non-finite inputs give
+ * unspecified codes. Bit-exact (the rounding decisions are exact). */
+moe_status moe_quantize_rows(int64_t rows, int32_t cols, int32_t src_dtype, const void* w,
+                             int32_t scale_dtype, int8_t* q, void* s, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_INT8_H */

@@ -1,0 +1,14 @@
+"""int8_weight_moe_amd: the forward pass of a mixture-of-experts feed-forward
+layer with int8 expert weights (the ExpertsInt8 scheme of the Jamba-1.5
+paper) on AMD MI355X (gfx950).
+
+The work is done by hand-written HIP kernels behind the C ABI of
+libmoe_int8.so (include/moe_int8.h); `ops` is a thin ctypes binding that
+takes torch tensors for device memory and streams.
+"""
+from ._lib import LIB_PATH, MoeError, load  # noqa: F401
+from .ops import (Int8Experts, MoeLayer, moe_combine, moe_expert_down, moe_expert_ffn, moe_expert_gate_up,  # noqa: F401
+                  moe_forward, moe_permute, moe_quantize_rows, moe_route, quantize_experts)
+
+__all__ = ["Int8Experts", "MoeLayer", "moe_route", "moe_permute", "moe_expert_ffn", "moe_expert_gate_up", "moe_expert_down", "moe_combine", "moe_forward",
+           "moe_quantize_rows", "quantize_experts", "MoeError", "load", "LIB_PATH"]

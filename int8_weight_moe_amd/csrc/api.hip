@@ -1,0 +1,333 @@
+// C ABI of libmoe_int8: argument validation, workspace layout and the
+// enqueueing of the kernels. Nothing here allocates memory or synchronises.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <atomic>
+
+#include "../../include/moe_int8.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+moe_status fail(moe_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+moe_status fail(moe_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+moe_status hip_fail(hipError_t e, const char* what) {
+  return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr size_t kAlign = 256;
+size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+// Rows at or below this many per expert (on average) go to the weight-streaming schedule.
+constexpr long kStreamRowsPerExpert = 48;
+
+moe_status check_shape(const moe_shape* s) {
+  if (!s) return fail(MOE_ERR_NULL, "shape is NULL");
+  if (s->T < 0) return fail(MOE_ERR_SHAPE, "T=%d must be >= 0", s->T);
+  if (s->d < 64 || s->d > 65536 || s->d % 64) return fail(MOE_ERR_SHAPE, "d=%d must be a multiple of 64 in [64, 65536]", s->d);
+  if (s->f < 64 || s->f > 131072 || s->f % 64) return fail(MOE_ERR_SHAPE, "f=%d must be a multiple of 64 in [64, 131072]", s->f);
+  if (s->E < 1 || s->E > 64) return fail(MOE_ERR_SHAPE, "E=%d must be in [1, 64]", s->E);
+  if (s->K < 1 || s->K > s->E || s->K > 8) return fail(MOE_ERR_SHAPE, "K=%d must be in [1, min(E, 8)]", s->K);
+  if ((long)s->T * s->K > (1L << 26)) return fail(MOE_ERR_SHAPE, "T*K=%ld exceeds 2^26", (long)s->T * s->K);
+  if (s->act_dtype != MOE_F32 && s->act_dtype != MOE_BF16) return fail(MOE_ERR_DTYPE, "act_dtype=%d", s->act_dtype);
+  if (s->scale_dtype != MOE_F32 && s->scale_dtype != MOE_BF16) return fail(MOE_ERR_DTYPE, "scale_dtype=%d", s->scale_dtype);
+  if (s->ffn_path < MOE_PATH_AUTO || s->ffn_path > MOE_PATH_TILED) return fail(MOE_ERR_SHAPE, "ffn_path=%d", s->ffn_path);
+  return MOE_OK;
+}
+
+#define REQUIRE_PTR(p)                                                         \
+  do {                                                                         \
+    if (!(p)) return fail(MOE_ERR_NULL, "%s is NULL", #p);                     \
+    if (!aligned16(p)) return fail(MOE_ERR_ALIGN, "%s is not 16-byte aligned", #p); \
+  } while (0)
+
+struct WsLayout {
+  size_t ids, w, offsets, sorted, s2r, h, y_rows, total;
+};
+
+WsLayout forward_layout(const moe_shape* s) {
+  const size_t S = (size_t)s->T * s->K;
+  WsLayout L;
+  size_t o = 0;
+  L.ids = o;     o += round_up(S * 4);
+  L.w = o;       o += round_up(S * 4);
+  L.offsets = o; o += round_up((s->E + 1) * 4);
+  L.sorted = o;  o += round_up(S * 4);
+  L.s2r = o;     o += round_up(S * 4);
+  L.h = o;       o += round_up(S * (size_t)s->f * 2);
+  L.y_rows = o;  o += round_up(S * (size_t)s->d * 4);
+  L.total = o;
+  return L;
+}
+
+size_t ffn_ws_bytes(const moe_shape* s) { return round_up((size_t)s->T * s->K * (size_t)s->f * 2); }
+
+bool use_stream(const moe_shape* s) {
+  if (s->ffn_path == MOE_PATH_STREAM) return true;
+  if (s->ffn_path == MOE_PATH_TILED) return false;
+  return (long)s->T * s->K <= kStreamRowsPerExpert * s->E;
+}
+
+moe::FfnArgs ffn_args(const moe_shape* s, const void* x, const int32_t* offsets, const int32_t* sorted_slots,
+                      const int8_t* w_gate, const int8_t* w_up, const int8_t* w_down, const void* s_gate,
+                      const void* s_up, const void* s_down, float* y_rows, __bf16* h) {
+  moe::FfnArgs a;
+  a.x = x;
+  a.act_bf16 = s->act_dtype == MOE_BF16;
+  a.scale_bf16 = s->scale_dtype == MOE_BF16;
+  a.offsets = offsets;
+  a.sorted_slots = sorted_slots;
+  a.w_gate = w_gate;
+  a.w_up = w_up;
+  a.w_down = w_down;
+  a.s_gate = s_gate;
+  a.s_up = s_up;
+  a.s_down = s_down;
+  a.h = h;
+  a.y_rows = y_rows;
+  a.T = s->T;
+  a.d = s->d;
+  a.f = s->f;
+  a.E = s->E;
+  a.K = s->K;
+  a.S = s->T * s->K;
+  return a;
+}
+
+moe_status run_gate_up(const moe_shape* s, const moe::FfnArgs& a, hipStream_t stream) {
+  const hipError_t e = use_stream(s) ? moe::launch_stream_gate_up(a, stream) : moe::launch_tiled_gate_up(a, stream);
+  if (e != hipSuccess) return hip_fail(e, "gate/up launch");
+  return MOE_OK;
+}
+
+moe_status run_down(const moe_shape* s, const moe::FfnArgs& a, hipStream_t stream) {
+  const hipError_t e = use_stream(s) ? moe::launch_stream_down(a, stream) : moe::launch_tiled_down(a, stream);
+  if (e != hipSuccess) return hip_fail(e, "down launch");
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char* moe_status_str(moe_status st) {
+  switch (st) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_NULL: return "null pointer";
+    case MOE_ERR_SHAPE: return "unsupported shape";
+    case MOE_ERR_DTYPE: return "unknown dtype";
+    case MOE_ERR_ALIGN: return "misaligned pointer";
+    case MOE_ERR_WORKSPACE: return "workspace too small";
+    case MOE_ERR_UNSUPPORTED: return "unsupported request";
+    case MOE_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* moe_last_error(void) { return g_err; }
+
+moe_status moe_workspace_size(const moe_shape* shape, size_t* bytes) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (!bytes) return fail(MOE_ERR_NULL, "bytes is NULL");
+  *bytes = forward_layout(shape).total;
+  return MOE_OK;
+}
+
+moe_status moe_ffn_workspace_size(const moe_shape* shape, size_t* bytes) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (!bytes) return fail(MOE_ERR_NULL, "bytes is NULL");
+  *bytes = ffn_ws_bytes(shape);
+  return MOE_OK;
+}
+
+moe_status moe_route(const moe_shape* s, const void* x, const void* router_w, const float* router_bias,
+                     int32_t* topk_ids, float* topk_w, hipStream_t stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  REQUIRE_PTR(x);
+  REQUIRE_PTR(router_w);
+  REQUIRE_PTR(topk_ids);
+  REQUIRE_PTR(topk_w);
+  if (router_bias && !aligned16(router_bias)) return fail(MOE_ERR_ALIGN, "router_bias is not 16-byte aligned");
+  if (s->T == 0) return MOE_OK;
+  const hipError_t e = moe::launch_router(x, router_w, router_bias, s->T, s->d, s->E, s->K,
+                                          s->act_dtype == MOE_BF16, topk_ids, topk_w, stream);
+  if (e != hipSuccess) return hip_fail(e, "router launch");
+  return MOE_OK;
+}
+
+moe_status moe_permute(const moe_shape* s, const int32_t* topk_ids, int32_t* expert_offsets,
+                       int32_t* sorted_slots, int32_t* slot_to_row, hipStream_t stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  REQUIRE_PTR(topk_ids);
+  REQUIRE_PTR(expert_offsets);
+  REQUIRE_PTR(sorted_slots);
+  REQUIRE_PTR(slot_to_row);
+  if (s->T == 0) return MOE_OK;
+  const hipError_t e = moe::launch_permute(topk_ids, s->T * s->K, s->E, expert_offsets, sorted_slots,
+                                           slot_to_row, stream);
+  if (e != hipSuccess) return hip_fail(e, "permute launch");
+  return MOE_OK;
+}
+
+moe_status moe_expert_ffn(const moe_shape* s, const void* x, const int32_t* expert_offsets,
+                          const int32_t* sorted_slots, const int8_t* w_gate, const int8_t* w_up,
+                          const int8_t* w_down, const void* s_gate, const void* s_up, const void* s_down,
+                          float* y_rows, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  REQUIRE_PTR(x);
+  REQUIRE_PTR(expert_offsets);
+  REQUIRE_PTR(sorted_slots);
+  REQUIRE_PTR(w_gate);
+  REQUIRE_PTR(w_up);
+  REQUIRE_PTR(w_down);
+  REQUIRE_PTR(s_gate);
+  REQUIRE_PTR(s_up);
+  REQUIRE_PTR(s_down);
+  REQUIRE_PTR(y_rows);
+  REQUIRE_PTR(workspace);
+  const size_t need = ffn_ws_bytes(s);
+  if (workspace_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "workspace_bytes=%zu < required %zu", workspace_bytes, need);
+  if (s->T == 0) return MOE_OK;
+  const moe::FfnArgs a = ffn_args(s, x, expert_offsets, sorted_slots, w_gate, w_up, w_down, s_gate, s_up, s_down,
+                                  y_rows, static_cast<__bf16*>(workspace));
+  st = run_gate_up(s, a, stream);
+  if (st != MOE_OK) return st;
+  return run_down(s, a, stream);
+}
+
+moe_status moe_expert_gate_up(const moe_shape* s, const void* x, const int32_t* expert_offsets,
+                              const int32_t* sorted_slots, const int8_t* w_gate, const int8_t* w_up,
+                              const void* s_gate, const void* s_up, void* h, hipStream_t stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  REQUIRE_PTR(x);
+  REQUIRE_PTR(expert_offsets);
+  REQUIRE_PTR(sorted_slots);
+  REQUIRE_PTR(w_gate);
+  REQUIRE_PTR(w_up);
+  REQUIRE_PTR(s_gate);
+  REQUIRE_PTR(s_up);
+  REQUIRE_PTR(h);
+  if (s->T == 0) return MOE_OK;
+  const moe::FfnArgs a = ffn_args(s, x, expert_offsets, sorted_slots, w_gate, w_up, nullptr, s_gate, s_up, nullptr,
+                                  nullptr, static_cast<__bf16*>(h));
+  return run_gate_up(s, a, stream);
+}
+
+moe_status moe_expert_down(const moe_shape* s, const void* h, const int32_t* expert_offsets, const int8_t* w_down,
+                           const void* s_down, float* y_rows, hipStream_t stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  REQUIRE_PTR(h);
+  REQUIRE_PTR(expert_offsets);
+  REQUIRE_PTR(w_down);
+  REQUIRE_PTR(s_down);
+  REQUIRE_PTR(y_rows);
+  if (s->T == 0) return MOE_OK;
+  const moe::FfnArgs a = ffn_args(s, nullptr, expert_offsets, nullptr, nullptr, nullptr, w_down, nullptr, nullptr,
+                                  s_down, y_rows, static_cast<__bf16*>(const_cast<void*>(h)));
+  return run_down(s, a, stream);
+}
+
+moe_status moe_combine(const moe_shape* s, const float* y_rows, const int32_t* slot_to_row,
+                       const float* topk_w, void* y, hipStream_t stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  REQUIRE_PTR(y_rows);
+  REQUIRE_PTR(slot_to_row);
+  REQUIRE_PTR(topk_w);
+  REQUIRE_PTR(y);
+  if (s->T == 0) return MOE_OK;
+  const hipError_t e = moe::launch_combine(y_rows, slot_to_row, topk_w, s->T, s->d, s->K,
+                                           s->act_dtype == MOE_BF16, y, stream);
+  if (e != hipSuccess) return hip_fail(e, "combine launch");
+  return MOE_OK;
+}
+
+moe_status moe_forward(const moe_shape* s, const void* x, const void* router_w, const float* router_bias,
+                       const int8_t* w_gate, const int8_t* w_up, const int8_t* w_down, const void* s_gate,
+                       const void* s_up, const void* s_down, void* y, int32_t* topk_ids_out, float* topk_w_out,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  REQUIRE_PTR(x);
+  REQUIRE_PTR(router_w);
+  REQUIRE_PTR(w_gate);
+  REQUIRE_PTR(w_up);
+  REQUIRE_PTR(w_down);
+  REQUIRE_PTR(s_gate);
+  REQUIRE_PTR(s_up);
+  REQUIRE_PTR(s_down);
+  REQUIRE_PTR(y);
+  REQUIRE_PTR(workspace);
+  if (router_bias && !aligned16(router_bias)) return fail(MOE_ERR_ALIGN, "router_bias is not 16-byte aligned");
+  if (topk_ids_out && !aligned16(topk_ids_out)) return fail(MOE_ERR_ALIGN, "topk_ids_out is not 16-byte aligned");
+  if (topk_w_out && !aligned16(topk_w_out)) return fail(MOE_ERR_ALIGN, "topk_w_out is not 16-byte aligned");
+  const WsLayout L = forward_layout(s);
+  if (workspace_bytes < L.total)
+    return fail(MOE_ERR_WORKSPACE, "workspace_bytes=%zu < required %zu", workspace_bytes, L.total);
+  if (s->T == 0) return MOE_OK;
+
+  char* ws = static_cast<char*>(workspace);
+  int32_t* ids = topk_ids_out ? topk_ids_out : reinterpret_cast<int32_t*>(ws + L.ids);
+  float* wts = topk_w_out ? topk_w_out : reinterpret_cast<float*>(ws + L.w);
+  int32_t* offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
+  int32_t* sorted = reinterpret_cast<int32_t*>(ws + L.sorted);
+  int32_t* s2r = reinterpret_cast<int32_t*>(ws + L.s2r);
+  __bf16* h = reinterpret_cast<__bf16*>(ws + L.h);
+  float* y_rows = reinterpret_cast<float*>(ws + L.y_rows);
+
+  hipError_t e = moe::launch_router(x, router_w, router_bias, s->T, s->d, s->E, s->K, s->act_dtype == MOE_BF16,
+                                    ids, wts, stream);
+  if (e != hipSuccess) return hip_fail(e, "router launch");
+  e = moe::launch_permute(ids, s->T * s->K, s->E, offsets, sorted, s2r, stream);
+  if (e != hipSuccess) return hip_fail(e, "permute launch");
+  const moe::FfnArgs a = ffn_args(s, x, offsets, sorted, w_gate, w_up, w_down, s_gate, s_up, s_down, y_rows, h);
+  st = run_gate_up(s, a, stream);
+  if (st != MOE_OK) return st;
+  st = run_down(s, a, stream);
+  if (st != MOE_OK) return st;
+  e = moe::launch_combine(y_rows, s2r, wts, s->T, s->d, s->K, s->act_dtype == MOE_BF16, y, stream);
+  if (e != hipSuccess) return hip_fail(e, "combine launch");
+  return MOE_OK;
+}
+
+moe_status moe_quantize_rows(int64_t rows, int32_t cols, int32_t src_dtype, const void* w, int32_t scale_dtype,
+                             int8_t* q, void* s, hipStream_t stream) {
+  if (rows < 0 || rows > 0x7fffffffL) return fail(MOE_ERR_SHAPE, "rows=%ld must be in [0, 2^31)", (long)rows);
+  if (cols < 16 || cols > (1 << 20) || cols % 16) return fail(MOE_ERR_SHAPE, "cols=%d must be a multiple of 16 in [16, 2^20]", cols);
+  if (src_dtype != MOE_F32 && src_dtype != MOE_BF16) return fail(MOE_ERR_DTYPE, "src_dtype=%d", src_dtype);
+  if (scale_dtype != MOE_F32 && scale_dtype != MOE_BF16) return fail(MOE_ERR_DTYPE, "scale_dtype=%d", scale_dtype);
+  REQUIRE_PTR(w);
+  REQUIRE_PTR(q);
+  if (!s) return fail(MOE_ERR_NULL, "s is NULL");
+  if ((reinterpret_cast<uintptr_t>(s) & 3u) != 0) return fail(MOE_ERR_ALIGN, "s is not 4-byte aligned");
+  if (rows == 0) return MOE_OK;
+  const hipError_t e = moe::launch_quantize_rows(rows, cols, src_dtype == MOE_BF16, w, scale_dtype == MOE_BF16, q,
+                                                 s, stream);
+  if (e != hipSuccess) return hip_fail(e, "quantize launch");
+  return MOE_OK;
+}
+
+}  // extern "C"

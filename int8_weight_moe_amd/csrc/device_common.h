@@ -1,0 +1,101 @@
+// Device-side helpers shared by the gfx950 kernels of libmoe_int8.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- MFMA
+// 16x16x32 bf16 MFMA (gfx950). Operand lane layout: lane l supplies row
+// (l % 16) of its operand with 8 reduction elements; lanes l/16 = 0..3 supply
+// four disjoint groups of 8 along the reduction axis. Any consistent
+// assignment of reduction indices to (lane group, element) works, because the
+// instruction sums over all 32. Result: lane l holds C[4*(l/16) + i][l % 16],
+// i = 0..3, where rows come from operand a and columns from operand b.
+__device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// 16x16x4 fp32 MFMA: lane l supplies row (l % 16), reduction index (l / 16).
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------- conversions
+// Eight int8 codes (two dwords, byte 0 first) -> eight bf16 values. Exact: a
+// code has at most 8 significant bits. Compiles to one sign-extending
+// byte->fp32 convert per code and one packed fp32->bf16 convert per pair.
+__device__ __forceinline__ bf16x8 i8x8_to_bf16(uint32_t lo, uint32_t hi) {
+  bf16x8 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = (__bf16)(float)(int8_t)(lo >> (8 * i));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[4 + i] = (__bf16)(float)(int8_t)(hi >> (8 * i));
+  return r;
+}
+
+__device__ __forceinline__ bf16x8 f32x8_to_bf16(float4 a, float4 b) {
+  bf16x8 r;
+  r[0] = (__bf16)a.x; r[1] = (__bf16)a.y; r[2] = (__bf16)a.z; r[3] = (__bf16)a.w;
+  r[4] = (__bf16)b.x; r[5] = (__bf16)b.y; r[6] = (__bf16)b.z; r[7] = (__bf16)b.w;
+  return r;
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) {
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+
+// Scale value of either dtype as fp32 (bf16 -> fp32 is exact).
+template <bool kScaleBf16>
+__device__ __forceinline__ float load_scale(const void* s, long idx) {
+  if constexpr (kScaleBf16) {
+    return bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(s)[idx]);
+  } else {
+    return reinterpret_cast<const float*>(s)[idx];
+  }
+}
+
+// SiLU in fp32: z / (1 + exp(-z)).
+__device__ __forceinline__ float silu(float z) {
+  return z / (1.0f + __expf(-z));
+}
+
+// ---------------------------------------------------------------- activation loads
+// Sixteen consecutive activations starting at p, as two bf16x8 (elements 0-7, 8-15).
+template <typename Act>
+struct Act16;
+
+template <>
+struct Act16<__bf16> {
+  static __device__ __forceinline__ void load(const __bf16* p, bf16x8& a0, bf16x8& a1) {
+    const uint4* q = reinterpret_cast<const uint4*>(p);
+    a0 = as_bf16x8(q[0]);
+    a1 = as_bf16x8(q[1]);
+  }
+};
+
+template <>
+struct Act16<float> {
+  static __device__ __forceinline__ void load(const float* p, bf16x8& a0, bf16x8& a1) {
+    const float4* q = reinterpret_cast<const float4*>(p);
+    a0 = f32x8_to_bf16(q[0], q[1]);
+    a1 = f32x8_to_bf16(q[2], q[3]);
+  }
+};
+
+__device__ __forceinline__ bf16x8 zero_bf16x8() {
+  return as_bf16x8(make_uint4(0, 0, 0, 0));
+}
+
+}  // namespace moe

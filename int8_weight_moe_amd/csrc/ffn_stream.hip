@@ -1,0 +1,233 @@
+// Expert FFN, weight-streaming schedule (few rows per expert: decode).
+//
+// With a handful of tokens per expert the layer is bound by reading the int8
+// weights from HBM once (the paper's serving note: MoE/MLP layers are
+// I/O-bound, and ExpertsInt8 moves the weights from HBM at half the bytes of
+// BF16). Each wave owns one (expert, group of 16*NG output channels) item and
+// runs the full reduction for all of the expert's rows (up to 16*RB per pass):
+//   - the weight rows of its channels stream from HBM in 64-byte pieces per
+//     channel and step (lane l: channel l%16, bytes 16*(l/16)..+16), with the
+//     loads of the next P-1 steps in flight;
+//   - the int8 codes become bf16 in registers (exact) and feed 16x16x32 bf16
+//     MFMA, with the channels as MFMA rows and the tokens as MFMA columns;
+//   - a 64-wide step is two MFMAs: code bytes 0-7 of each lane pair with
+//     activation elements 0-7 of the same lane group, bytes 8-15 with 8-15.
+// Items are numbered over the experts that received rows only, so the grid
+// has no idle waves for untouched experts.
+// Gate/up pass: g and u accumulate side by side; the epilogue applies the
+// per-channel scales and SwiGLU and stores h (bf16). Down pass: the epilogue
+// applies the down scale and stores y_rows (fp32).
+#include "device_common.h"
+#include "kernels.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kStreamWaves = 4;
+
+template <bool kGateUp, typename Act, bool kScaleBf16, int NG, int RB, int P>
+__global__ __launch_bounds__(kStreamWaves * kWave) void ffn_stream_kernel(
+    const Act* __restrict__ X, const int32_t* __restrict__ sorted_slots, int topk,
+    const int8_t* __restrict__ W0, const int8_t* __restrict__ W1, const void* __restrict__ S0,
+    const void* __restrict__ S1, const int32_t* __restrict__ offsets, int E, int N, int Kd,
+    void* __restrict__ out) {
+  constexpr int NMAT = kGateUp ? 2 : 1;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int li = lane & 15;
+  const int lg = lane >> 4;
+
+  // ---- item -> (expert among the touched ones, channel group)
+  const int gpe = N / (16 * NG);
+  const int item = blockIdx.x * kStreamWaves + wave;
+  const int te = item / gpe;
+  const int grp = item - te * gpe;
+  int e = -1, row0 = 0, nrows = 0;
+  {
+    int seen = 0;
+    for (int x = 0; x < E; ++x) {
+      const int o0 = offsets[x], o1 = offsets[x + 1];
+      if (o1 > o0) {
+        if (seen == te) {
+          e = x;
+          row0 = o0;
+          nrows = o1 - o0;
+          break;
+        }
+        ++seen;
+      }
+    }
+  }
+  if (e < 0) return;
+
+  const int ch_base = grp * 16 * NG;
+  const int8_t* wp[NG][NMAT];
+#pragma unroll
+  for (int ng = 0; ng < NG; ++ng) {
+    const long ch = (long)e * N + ch_base + ng * 16 + li;
+    wp[ng][0] = W0 + ch * Kd + 16 * lg;
+    if constexpr (kGateUp) wp[ng][1] = W1 + ch * Kd + 16 * lg;
+  }
+  // per-lane scales of the 4 channels this lane holds in the result
+  float sc[NG][NMAT][4];
+#pragma unroll
+  for (int ng = 0; ng < NG; ++ng) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const long ch = (long)e * N + ch_base + ng * 16 + 4 * lg + r;
+      sc[ng][0][r] = load_scale<kScaleBf16>(S0, ch);
+      if constexpr (kGateUp) sc[ng][1][r] = load_scale<kScaleBf16>(S1, ch);
+    }
+  }
+
+  const int nsteps = Kd >> 6;
+
+  for (int p0 = 0; p0 < nrows; p0 += 16 * RB) {
+    const int prow = min(16 * RB, nrows - p0);
+    const int nrb = (prow + 15) >> 4;
+    const Act* ap[RB];
+    bool aok[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const int r = p0 + rb * 16 + li;
+      aok[rb] = r < nrows;
+      long src = 0;
+      if (aok[rb]) {
+        if constexpr (kGateUp) {
+          src = (long)(sorted_slots[row0 + r] / topk) * Kd;
+        } else {
+          src = (long)(row0 + r) * Kd;
+        }
+      }
+      ap[rb] = X + src + 16 * lg;
+    }
+
+    f32x4 acc[RB][NG][NMAT];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int ng = 0; ng < NG; ++ng)
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m) acc[rb][ng][m] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    uint4 bw[P][NG][NMAT];
+    bf16x8 av[P][RB][2];
+
+    auto load_step = [&](int slot_unused, int s, uint4 (&b)[NG][NMAT], bf16x8 (&a)[RB][2]) {
+      (void)slot_unused;
+      const long off = (long)s * 64;
+#pragma unroll
+      for (int ng = 0; ng < NG; ++ng)
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m) b[ng][m] = *reinterpret_cast<const uint4*>(wp[ng][m] + off);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        if (rb < nrb && aok[rb]) {
+          Act16<Act>::load(ap[rb] + off, a[rb][0], a[rb][1]);
+        } else {
+          a[rb][0] = zero_bf16x8();
+          a[rb][1] = zero_bf16x8();
+        }
+      }
+    };
+    auto compute_step = [&](const uint4 (&b)[NG][NMAT], const bf16x8 (&a)[RB][2]) {
+#pragma unroll
+      for (int ng = 0; ng < NG; ++ng) {
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m) {
+          const bf16x8 w_lo = i8x8_to_bf16(b[ng][m].x, b[ng][m].y);
+          const bf16x8 w_hi = i8x8_to_bf16(b[ng][m].z, b[ng][m].w);
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) {
+            if (rb < nrb) {
+              acc[rb][ng][m] = mfma_bf16(w_lo, a[rb][0], acc[rb][ng][m]);
+              acc[rb][ng][m] = mfma_bf16(w_hi, a[rb][1], acc[rb][ng][m]);
+            }
+          }
+        }
+      }
+    };
+
+#pragma unroll
+    for (int j = 0; j < P - 1; ++j)
+      if (j < nsteps) load_step(j, j, bw[j], av[j]);
+    for (int s0 = 0; s0 < nsteps; s0 += P) {
+#pragma unroll
+      for (int j = 0; j < P; ++j) {
+        const int s = s0 + j;
+        const int sl = s + P - 1;
+        if (sl < nsteps) load_step((j + P - 1) % P, sl, bw[(j + P - 1) % P], av[(j + P - 1) % P]);
+        if (s < nsteps) compute_step(bw[j], av[j]);
+      }
+    }
+
+    // ---- epilogue: lane holds channels ch_base + ng*16 + 4*lg + r, row p0 + rb*16 + li
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const int r = p0 + rb * 16 + li;
+      if (rb < nrb && r < nrows) {
+        const long orow = (long)(row0 + r) * N;
+#pragma unroll
+        for (int ng = 0; ng < NG; ++ng) {
+          const int ch = ch_base + ng * 16 + 4 * lg;
+          if constexpr (kGateUp) {
+            bf16x4 hv;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const float g = acc[rb][ng][0][q] * sc[ng][0][q];
+              const float u = acc[rb][ng][1][q] * sc[ng][1][q];
+              hv[q] = (__bf16)(silu(g) * u);
+            }
+            *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(out) + orow + ch) = hv;
+          } else {
+            float4 yv;
+            yv.x = acc[rb][ng][0][0] * sc[ng][0][0];
+            yv.y = acc[rb][ng][0][1] * sc[ng][0][1];
+            yv.z = acc[rb][ng][0][2] * sc[ng][0][2];
+            yv.w = acc[rb][ng][0][3] * sc[ng][0][3];
+            *reinterpret_cast<float4*>(static_cast<float*>(out) + orow + ch) = yv;
+          }
+        }
+      }
+    }
+  }
+}
+
+template <bool kGateUp, typename Act, bool kScaleBf16>
+hipError_t launch_stream_pass(const FfnArgs& a, hipStream_t stream) {
+  constexpr int NG = 2, RB = 2, P = 3;
+  const int N = kGateUp ? a.f : a.d;
+  const int Kd = kGateUp ? a.d : a.f;
+  const int gpe = N / (16 * NG);
+  const long items = (long)a.E * gpe;
+  const dim3 grid((unsigned)((items + kStreamWaves - 1) / kStreamWaves));
+  const dim3 block(kStreamWaves * kWave);
+  if constexpr (kGateUp) {
+    hipLaunchKernelGGL((ffn_stream_kernel<true, Act, kScaleBf16, NG, RB, P>), grid, block, 0, stream,
+                       static_cast<const Act*>(a.x), a.sorted_slots, a.K, a.w_gate, a.w_up, a.s_gate, a.s_up,
+                       a.offsets, a.E, N, Kd, static_cast<void*>(a.h));
+  } else {
+    hipLaunchKernelGGL((ffn_stream_kernel<false, __bf16, kScaleBf16, NG, RB, P>), grid, block, 0, stream,
+                       static_cast<const __bf16*>(a.h), a.sorted_slots, a.K, a.w_down, nullptr, a.s_down,
+                       nullptr, a.offsets, a.E, N, Kd, static_cast<void*>(a.y_rows));
+  }
+  return hipGetLastError();
+}
+
+template <bool kGateUp>
+hipError_t dispatch_stream(const FfnArgs& a, hipStream_t stream) {
+  if (a.act_bf16) {
+    return a.scale_bf16 ? launch_stream_pass<kGateUp, __bf16, true>(a, stream)
+                        : launch_stream_pass<kGateUp, __bf16, false>(a, stream);
+  }
+  return a.scale_bf16 ? launch_stream_pass<kGateUp, float, true>(a, stream)
+                      : launch_stream_pass<kGateUp, float, false>(a, stream);
+}
+
+}  // namespace
+
+hipError_t launch_stream_gate_up(const FfnArgs& a, hipStream_t stream) { return dispatch_stream<true>(a, stream); }
+hipError_t launch_stream_down(const FfnArgs& a, hipStream_t stream) { return dispatch_stream<false>(a, stream); }
+
+}  // namespace moe

@@ -1,0 +1,49 @@
+// Launchers of the gfx950 kernels (host side). Arguments are validated by the
+// C ABI layer before any of these is called; each returns the HIP status of
+// its launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+hipError_t launch_router(const void* x, const void* router_w, const float* bias, int T, int d, int E, int K,
+                         bool act_bf16, int32_t* topk_ids, float* topk_w, hipStream_t stream);
+
+hipError_t launch_permute(const int32_t* ids, int S, int E, int32_t* offsets, int32_t* sorted_slots,
+                          int32_t* slot_to_row, hipStream_t stream);
+
+// Arguments of the expert FFN (both schedules).
+struct FfnArgs {
+  const void* x;              // [T, d] activations
+  bool act_bf16;              // x dtype
+  bool scale_bf16;            // scale dtype
+  const int32_t* offsets;     // [E + 1]
+  const int32_t* sorted_slots;  // [S]
+  const int8_t* w_gate;       // [E, f, d]
+  const int8_t* w_up;         // [E, f, d]
+  const int8_t* w_down;       // [E, d, f]
+  const void* s_gate;         // [E, f]
+  const void* s_up;           // [E, f]
+  const void* s_down;         // [E, d]
+  __bf16* h;                  // [S, f] scratch
+  float* y_rows;              // [S, d] out
+  int T, d, f, E, K, S;
+};
+
+// Weight-streaming schedule for few rows per expert (decode): gate/up pass
+// (x -> h) and down pass (h -> y_rows).
+hipError_t launch_stream_gate_up(const FfnArgs& a, hipStream_t stream);
+hipError_t launch_stream_down(const FfnArgs& a, hipStream_t stream);
+// Tiled MFMA schedule for many rows per expert (prefill).
+hipError_t launch_tiled_gate_up(const FfnArgs& a, hipStream_t stream);
+hipError_t launch_tiled_down(const FfnArgs& a, hipStream_t stream);
+
+hipError_t launch_combine(const float* y_rows, const int32_t* slot_to_row, const float* topk_w, int T, int d,
+                          int K, bool act_bf16, void* y, hipStream_t stream);
+
+hipError_t launch_quantize_rows(int64_t rows, int cols, bool src_bf16, const void* w, bool scale_bf16, int8_t* q,
+                                void* s, hipStream_t stream);
+
+}  // namespace moe

@@ -1,0 +1,170 @@
+// Router and top-K gate (Jamba-1.5 paper, "Model Architecture": a router picks
+// the top K of n experts for every token).
+//
+// One workgroup scores 16 tokens against every expert. The 8 waves split the
+// hidden dimension, each accumulating a 16x16 logit tile per block of 16
+// experts with MFMA (bf16 inputs: 16x16x32 bf16, products exact, fp32 sums;
+// fp32 inputs: 16x16x4 fp32). The partial tiles are summed through LDS in a
+// fixed wave order, so the logits do not depend on scheduling. Then each wave
+// takes two tokens: lane e holds logit e, K rounds of a wavefront argmax
+// (ties to the lower expert index) pick the experts, and the gate weights are
+// the softmax renormalised over the chosen set,
+//   w_k = exp(l_k - l_max) / sum_j exp(l_j - l_max).
+#include "device_common.h"
+#include "kernels.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kRouterWaves = 8;
+constexpr int kRouterTokens = 16;
+constexpr int kMaxExperts = 64;
+
+template <typename Act>
+__device__ __forceinline__ void router_accumulate(const Act* __restrict__ x, const Act* __restrict__ wr,
+                                                  int T, int d, int E, int tok0, int wave, int lane,
+                                                  f32x4 (&acc)[4]) {
+  const int i = lane & 15;
+  const int g = lane >> 4;
+  const int tok = tok0 + i;
+  const bool tok_ok = tok < T;
+  const int EB = (E + 15) >> 4;
+  const int nchunks = d >> 5;  // 32 reduction elements per chunk
+  for (int c = wave; c < nchunks; c += kRouterWaves) {
+    const int kk = c * 32 + 8 * g;
+    if constexpr (sizeof(Act) == 2) {
+      bf16x8 a = tok_ok ? as_bf16x8(*reinterpret_cast<const uint4*>(x + (long)tok * d + kk)) : zero_bf16x8();
+#pragma unroll
+      for (int eb = 0; eb < 4; ++eb) {
+        if (eb < EB) {
+          const int e = eb * 16 + i;
+          bf16x8 b = (e < E) ? as_bf16x8(*reinterpret_cast<const uint4*>(wr + (long)e * d + kk)) : zero_bf16x8();
+          acc[eb] = mfma_bf16(a, b, acc[eb]);
+        }
+      }
+    } else {
+      float av[8];
+      {
+        float4 p0 = make_float4(0.f, 0.f, 0.f, 0.f), p1 = p0;
+        if (tok_ok) {
+          const float4* q = reinterpret_cast<const float4*>(x + (long)tok * d + kk);
+          p0 = q[0];
+          p1 = q[1];
+        }
+        av[0] = p0.x; av[1] = p0.y; av[2] = p0.z; av[3] = p0.w;
+        av[4] = p1.x; av[5] = p1.y; av[6] = p1.z; av[7] = p1.w;
+      }
+#pragma unroll
+      for (int eb = 0; eb < 4; ++eb) {
+        if (eb < EB) {
+          const int e = eb * 16 + i;
+          float4 p0 = make_float4(0.f, 0.f, 0.f, 0.f), p1 = p0;
+          if (e < E) {
+            const float4* q = reinterpret_cast<const float4*>(wr + (long)e * d + kk);
+            p0 = q[0];
+            p1 = q[1];
+          }
+          const float bv[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+#pragma unroll
+          for (int j = 0; j < 8; ++j) acc[eb] = mfma_f32(av[j], bv[j], acc[eb]);
+        }
+      }
+    }
+  }
+}
+
+// argmax over the wavefront of (value, index); ties to the lower index.
+__device__ __forceinline__ void wave_argmax(float& v, int& idx) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float ov = __shfl_xor(v, off);
+    const int oi = __shfl_xor(idx, off);
+    if (ov > v || (ov == v && oi < idx)) {
+      v = ov;
+      idx = oi;
+    }
+  }
+}
+
+template <typename Act>
+__global__ __launch_bounds__(kRouterWaves * kWave) void router_topk_kernel(
+    const Act* __restrict__ x, const Act* __restrict__ wr, const float* __restrict__ bias,
+    int T, int d, int E, int K, int32_t* __restrict__ topk_ids, float* __restrict__ topk_w) {
+  __shared__ float red[kRouterWaves][kRouterTokens][kMaxExperts];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int tok0 = blockIdx.x * kRouterTokens;
+
+  f32x4 acc[4];
+#pragma unroll
+  for (int eb = 0; eb < 4; ++eb) acc[eb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  router_accumulate<Act>(x, wr, T, d, E, tok0, wave, lane, acc);
+
+  // C[token 4*(l/16)+r][expert 16*eb + l%16]
+  const int EB = (E + 15) >> 4;
+#pragma unroll
+  for (int eb = 0; eb < 4; ++eb) {
+    if (eb < EB) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) red[wave][4 * (lane >> 4) + r][eb * 16 + (lane & 15)] = acc[eb][r];
+    }
+  }
+  __syncthreads();
+
+  for (int tl = wave; tl < kRouterTokens; tl += kRouterWaves) {
+    const int t = tok0 + tl;
+    if (t >= T) break;
+    float l = -INFINITY;
+    if (lane < E) {
+      float s = 0.f;
+#pragma unroll
+      for (int w = 0; w < kRouterWaves; ++w) s += red[w][tl][lane];
+      if (bias) s += bias[lane];
+      l = s;
+    }
+    float v = l;
+    float top = 0.f;
+    float den = 0.f;
+    float my_e = 0.f;   // this lane's exp(l_k - l_max) when lane == k
+    int my_id = 0;
+    bool chosen = false;
+    for (int k = 0; k < K; ++k) {
+      float bv = chosen ? -INFINITY : v;
+      int bi = lane;
+      wave_argmax(bv, bi);
+      if (k == 0) top = bv;
+      const float ek = __expf(bv - top);
+      den += ek;
+      if (lane == bi) chosen = true;
+      if (lane == k) {
+        my_e = ek;
+        my_id = bi;
+      }
+    }
+    if (lane < K) {
+      topk_ids[(long)t * K + lane] = my_id;
+      topk_w[(long)t * K + lane] = my_e / den;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_router(const void* x, const void* router_w, const float* bias, int T, int d, int E, int K,
+                         bool act_bf16, int32_t* topk_ids, float* topk_w, hipStream_t stream) {
+  if (T == 0) return hipSuccess;
+  const dim3 grid((T + kRouterTokens - 1) / kRouterTokens);
+  const dim3 block(kRouterWaves * kWave);
+  if (act_bf16) {
+    hipLaunchKernelGGL(router_topk_kernel<__bf16>, grid, block, 0, stream,
+                       static_cast<const __bf16*>(x), static_cast<const __bf16*>(router_w), bias, T, d, E, K,
+                       topk_ids, topk_w);
+  } else {
+    hipLaunchKernelGGL(router_topk_kernel<float>, grid, block, 0, stream, static_cast<const float*>(x),
+                       static_cast<const float*>(router_w), bias, T, d, E, K, topk_ids, topk_w);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

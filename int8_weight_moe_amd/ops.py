@@ -1,0 +1,248 @@
+"""Python binding of libmoe_int8: argument marshalling only.
+
+Each function takes torch tensors that already live on the current HIP device,
+allocates the outputs (torch is the memory and stream provider), and calls the
+C entry point of the same name on torch's current stream. Every step of the
+layer runs in the library's kernels.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+from typing import Optional
+
+import torch
+
+from . import _lib
+from ._lib import MOE_BF16, MOE_F32, MOE_PATH_AUTO, MOE_PATH_STREAM, MOE_PATH_TILED, MoeError, MoeShape  # noqa: F401
+
+_DT = {torch.float32: MOE_F32, torch.bfloat16: MOE_BF16}
+
+
+@dataclasses.dataclass
+class Int8Experts:
+    """ExpertsInt8 weights of one MoE layer: int8 codes plus per-output-channel scales.
+
+    q_gate, q_up [E, f, d] int8; q_down [E, d, f] int8; s_gate, s_up [E, f]; s_down [E, d]
+    (scales all fp32 or all bf16).
+    """
+    q_gate: torch.Tensor
+    q_up: torch.Tensor
+    q_down: torch.Tensor
+    s_gate: torch.Tensor
+    s_up: torch.Tensor
+    s_down: torch.Tensor
+
+    @property
+    def E(self) -> int:
+        return self.q_gate.shape[0]
+
+    @property
+    def f(self) -> int:
+        return self.q_gate.shape[1]
+
+    @property
+    def d(self) -> int:
+        return self.q_gate.shape[2]
+
+    @property
+    def scale_dtype(self) -> torch.dtype:
+        return self.s_gate.dtype
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libmoe_int8 must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dtype_code(dt: torch.dtype) -> int:
+    if dt not in _DT:
+        raise TypeError(f"unsupported dtype {dt}")
+    return _DT[dt]
+
+
+def make_shape(T: int, d: int, f: int, E: int, K: int, act: torch.dtype, scale: torch.dtype,
+               path: int = MOE_PATH_AUTO) -> MoeShape:
+    return MoeShape(T, d, f, E, K, _dtype_code(act), _dtype_code(scale), path)
+
+
+def _lib_handle():
+    return _lib.load()
+
+
+def workspace_size(shape: MoeShape) -> int:
+    lib = _lib_handle()
+    n = ctypes.c_size_t(0)
+    _lib.check(lib.moe_workspace_size(ctypes.byref(shape), ctypes.byref(n)))
+    return n.value
+
+
+def ffn_workspace_size(shape: MoeShape) -> int:
+    lib = _lib_handle()
+    n = ctypes.c_size_t(0)
+    _lib.check(lib.moe_ffn_workspace_size(ctypes.byref(shape), ctypes.byref(n)))
+    return n.value
+
+
+def moe_route(x: torch.Tensor, router_w: torch.Tensor, bias: Optional[torch.Tensor], K: int):
+    """Router + top-K gate. Returns (topk_ids int32 [T,K], topk_w fp32 [T,K])."""
+    lib = _lib_handle()
+    T, d = x.shape
+    E = router_w.shape[0]
+    shape = make_shape(T, d, 64, E, K, x.dtype, torch.float32)
+    ids = torch.empty((T, K), dtype=torch.int32, device=x.device)
+    w = torch.empty((T, K), dtype=torch.float32, device=x.device)
+    _lib.check(lib.moe_route(ctypes.byref(shape), _ptr(x), _ptr(router_w), _ptr(bias), _ptr(ids), _ptr(w),
+                             _stream()))
+    return ids, w
+
+
+def moe_permute(topk_ids: torch.Tensor, E: int):
+    """Returns (expert_offsets [E+1], sorted_slots [T*K], slot_to_row [T*K]), all int32."""
+    lib = _lib_handle()
+    T, K = topk_ids.shape
+    shape = MoeShape(T, 64, 64, E, K, MOE_BF16, MOE_BF16, MOE_PATH_AUTO)
+    dev = topk_ids.device
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    sorted_slots = torch.empty(T * K, dtype=torch.int32, device=dev)
+    slot_to_row = torch.empty(T * K, dtype=torch.int32, device=dev)
+    _lib.check(lib.moe_permute(ctypes.byref(shape), _ptr(topk_ids), _ptr(offsets), _ptr(sorted_slots),
+                               _ptr(slot_to_row), _stream()))
+    return offsets, sorted_slots, slot_to_row
+
+
+def moe_expert_ffn(x: torch.Tensor, expert_offsets: torch.Tensor, sorted_slots: torch.Tensor,
+                   experts: Int8Experts, K: int, path: int = MOE_PATH_AUTO,
+                   workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Expert SwiGLU FFNs on the permuted rows. Returns y_rows fp32 [T*K, d] (sorted-row order)."""
+    lib = _lib_handle()
+    T, d = x.shape
+    shape = make_shape(T, d, experts.f, experts.E, K, x.dtype, experts.scale_dtype, path)
+    y_rows = torch.empty((T * K, d), dtype=torch.float32, device=x.device)
+    need = ffn_workspace_size(shape)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=x.device)
+    _lib.check(lib.moe_expert_ffn(
+        ctypes.byref(shape), _ptr(x), _ptr(expert_offsets), _ptr(sorted_slots), _ptr(experts.q_gate),
+        _ptr(experts.q_up), _ptr(experts.q_down), _ptr(experts.s_gate), _ptr(experts.s_up),
+        _ptr(experts.s_down), _ptr(y_rows), _ptr(workspace), ctypes.c_size_t(workspace.numel()), _stream()))
+    return y_rows
+
+
+def moe_expert_gate_up(x: torch.Tensor, expert_offsets: torch.Tensor, sorted_slots: torch.Tensor,
+                       experts: Int8Experts, K: int, path: int = MOE_PATH_AUTO,
+                       h: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Gate/up pass: h [T*K, f] bf16 (sorted-row order)."""
+    lib = _lib_handle()
+    T, d = x.shape
+    shape = make_shape(T, d, experts.f, experts.E, K, x.dtype, experts.scale_dtype, path)
+    if h is None:
+        h = torch.empty((T * K, experts.f), dtype=torch.bfloat16, device=x.device)
+    _lib.check(lib.moe_expert_gate_up(
+        ctypes.byref(shape), _ptr(x), _ptr(expert_offsets), _ptr(sorted_slots), _ptr(experts.q_gate),
+        _ptr(experts.q_up), _ptr(experts.s_gate), _ptr(experts.s_up), _ptr(h), _stream()))
+    return h
+
+
+def moe_expert_down(h: torch.Tensor, expert_offsets: torch.Tensor, experts: Int8Experts, T: int, K: int,
+                    act: torch.dtype = torch.bfloat16, path: int = MOE_PATH_AUTO,
+                    y_rows: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Down pass: y_rows [T*K, d] fp32 from h [T*K, f] bf16."""
+    lib = _lib_handle()
+    shape = make_shape(T, experts.d, experts.f, experts.E, K, act, experts.scale_dtype, path)
+    if y_rows is None:
+        y_rows = torch.empty((T * K, experts.d), dtype=torch.float32, device=h.device)
+    _lib.check(lib.moe_expert_down(ctypes.byref(shape), _ptr(h), _ptr(expert_offsets), _ptr(experts.q_down),
+                                   _ptr(experts.s_down), _ptr(y_rows), _stream()))
+    return y_rows
+
+
+def moe_combine(y_rows: torch.Tensor, slot_to_row: torch.Tensor, topk_w: torch.Tensor,
+                out_dtype: torch.dtype) -> torch.Tensor:
+    """y[t] = sum_k topk_w[t,k] * y_rows[slot_to_row[t*K+k]]. Returns y [T, d] in out_dtype."""
+    lib = _lib_handle()
+    T, K = topk_w.shape
+    d = y_rows.shape[1]
+    shape = make_shape(T, d, 64, max(K, 1), K, out_dtype, torch.float32)
+    y = torch.empty((T, d), dtype=out_dtype, device=y_rows.device)
+    _lib.check(lib.moe_combine(ctypes.byref(shape), _ptr(y_rows), _ptr(slot_to_row), _ptr(topk_w), _ptr(y),
+                               _stream()))
+    return y
+
+
+class MoeLayer:
+    """A resident MoE layer: router weights, int8 experts and a reusable workspace."""
+
+    def __init__(self, router_w: torch.Tensor, bias: Optional[torch.Tensor], experts: Int8Experts, K: int):
+        self.router_w = router_w
+        self.bias = bias
+        self.experts = experts
+        self.K = K
+        self._ws = None
+
+    def workspace(self, shape: MoeShape) -> torch.Tensor:
+        need = max(workspace_size(shape), 256)
+        if self._ws is None or self._ws.numel() < need:
+            self._ws = torch.empty(need, dtype=torch.uint8, device=self.router_w.device)
+        return self._ws
+
+    def forward(self, x: torch.Tensor, path: int = MOE_PATH_AUTO, y: Optional[torch.Tensor] = None,
+                ids: Optional[torch.Tensor] = None, w: Optional[torch.Tensor] = None):
+        return moe_forward(x, self.router_w, self.bias, self.experts, self.K, path=path, y=y, ids=ids, w=w,
+                           workspace=self.workspace(self.shape(x, path)))
+
+    def shape(self, x: torch.Tensor, path: int = MOE_PATH_AUTO) -> MoeShape:
+        e = self.experts
+        return make_shape(x.shape[0], x.shape[1], e.f, e.E, self.K, x.dtype, e.scale_dtype, path)
+
+
+def moe_forward(x: torch.Tensor, router_w: torch.Tensor, bias: Optional[torch.Tensor], experts: Int8Experts,
+                K: int, path: int = MOE_PATH_AUTO, y: Optional[torch.Tensor] = None,
+                ids: Optional[torch.Tensor] = None, w: Optional[torch.Tensor] = None,
+                workspace: Optional[torch.Tensor] = None):
+    """The whole layer. Returns (y [T, d] in x.dtype, topk_ids [T, K], topk_w [T, K])."""
+    lib = _lib_handle()
+    T, d = x.shape
+    shape = make_shape(T, d, experts.f, experts.E, K, x.dtype, experts.scale_dtype, path)
+    dev = x.device
+    if y is None:
+        y = torch.empty((T, d), dtype=x.dtype, device=dev)
+    if ids is None:
+        ids = torch.empty((T, K), dtype=torch.int32, device=dev)
+    if w is None:
+        w = torch.empty((T, K), dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = torch.empty(max(workspace_size(shape), 256), dtype=torch.uint8, device=dev)
+    _lib.check(lib.moe_forward(
+        ctypes.byref(shape), _ptr(x), _ptr(router_w), _ptr(bias), _ptr(experts.q_gate), _ptr(experts.q_up),
+        _ptr(experts.q_down), _ptr(experts.s_gate), _ptr(experts.s_up), _ptr(experts.s_down), _ptr(y), _ptr(ids),
+        _ptr(w), _ptr(workspace), ctypes.c_size_t(workspace.numel()), _stream()))
+    return y, ids, w
+
+
+def moe_quantize_rows(w: torch.Tensor, scale_dtype: torch.dtype):
+    """ExpertsInt8 quantizer on the GPU: w [..., cols] (fp32/bf16) -> (q int8 [..., cols], s [...])."""
+    lib = _lib_handle()
+    cols = w.shape[-1]
+    rows = w.numel() // cols
+    q = torch.empty(w.shape, dtype=torch.int8, device=w.device)
+    s = torch.empty(w.shape[:-1], dtype=scale_dtype, device=w.device)
+    _lib.check(lib.moe_quantize_rows(ctypes.c_int64(rows), ctypes.c_int32(cols), _dtype_code(w.dtype), _ptr(w),
+                                     _dtype_code(scale_dtype), _ptr(q), _ptr(s), _stream()))
+    return q, s
+
+
+def quantize_experts(w_gate: torch.Tensor, w_up: torch.Tensor, w_down: torch.Tensor,
+                     scale_dtype: torch.dtype) -> Int8Experts:
+    """Quantize a layer's unquantized (out, in) expert weights with moe_quantize_rows."""
+    qg, sg = moe_quantize_rows(w_gate, scale_dtype)
+    qu, su = moe_quantize_rows(w_up, scale_dtype)
+    qd, sd = moe_quantize_rows(w_down, scale_dtype)
+    return Int8Experts(qg, qu, qd, sg, su, sd)

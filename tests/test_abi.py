@@ -1,0 +1,129 @@
+"""Host-side checks of the C ABI (no GPU needed: nothing here launches a kernel).
+
+  * libmoe_int8.so loads and exports every function include/moe_int8.h declares;
+  * the header's enums agree with the binding's constants;
+  * argument validation returns the documented status before any launch
+    (null and misaligned pointers, bad shapes and dtypes, small workspace);
+  * workspace sizes follow the documented layout;
+  * T = 0 is accepted and enqueues nothing.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from int8_weight_moe_amd import _lib
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "moe_int8.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(moe_[a-z_0-9]+)\s*\(", text, flags=re.M)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    declared = _declared_functions()
+    assert set(declared) == set(_lib.EXPORTS), declared
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_header_constants_match_binding():
+    text = open(HEADER).read()
+    for name, val in (("MOE_OK", 0), ("MOE_ERR_NULL", 1), ("MOE_ERR_SHAPE", 2), ("MOE_ERR_DTYPE", 3),
+                      ("MOE_ERR_ALIGN", 4), ("MOE_ERR_WORKSPACE", 5), ("MOE_ERR_UNSUPPORTED", 6),
+                      ("MOE_ERR_HIP", 7), ("MOE_F32", 0), ("MOE_BF16", 1), ("MOE_PATH_AUTO", 0),
+                      ("MOE_PATH_STREAM", 1), ("MOE_PATH_TILED", 2)):
+        assert re.search(rf"\b{name}\s*=\s*{val}\b", text), name
+    assert ctypes.sizeof(_lib.MoeShape) == 32
+
+
+def test_status_strings(lib):
+    for st in range(8):
+        assert lib.moe_status_str(st)
+    assert lib.moe_abi_version() == 1
+
+
+def _shape(**kw):
+    base = dict(T=32, d=256, f=512, E=16, K=2, act_dtype=1, scale_dtype=1, ffn_path=0)
+    base.update(kw)
+    return _lib.MoeShape(**base)
+
+
+# fake but 256-aligned "device" addresses: validation never dereferences them
+A = ctypes.c_void_p(0x10000)
+B = ctypes.c_void_p(0x20000)
+MIS = ctypes.c_void_p(0x10008)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(T=-1), 2), (dict(d=100), 2), (dict(d=0), 2), (dict(f=96), 2), (dict(E=0), 2), (dict(E=65), 2),
+    (dict(K=0), 2), (dict(K=17), 2), (dict(E=4, K=5), 2), (dict(K=9, E=16), 2), (dict(act_dtype=5), 3),
+    (dict(scale_dtype=-1), 3), (dict(ffn_path=3), 2),
+])
+def test_shape_validation(lib, kw, status):
+    n = ctypes.c_size_t(0)
+    s = _shape(**kw)
+    assert lib.moe_workspace_size(ctypes.byref(s), ctypes.byref(n)) == status
+    assert lib.moe_last_error()
+    assert lib.moe_route(ctypes.byref(s), A, A, None, A, A, None) == status
+
+
+def test_null_and_alignment(lib):
+    s = _shape()
+    assert lib.moe_route(None, A, A, None, A, A, None) == 1
+    assert lib.moe_route(ctypes.byref(s), None, A, None, A, A, None) == 1
+    assert b"x is NULL" in lib.moe_last_error()
+    assert lib.moe_route(ctypes.byref(s), MIS, A, None, A, A, None) == 4
+    assert lib.moe_route(ctypes.byref(s), A, A, MIS, A, A, None) == 4
+    assert lib.moe_permute(ctypes.byref(s), A, None, A, A, None) == 1
+    assert lib.moe_combine(ctypes.byref(s), A, A, A, MIS, None) == 4
+    args = [A] * 10
+    assert lib.moe_expert_ffn(ctypes.byref(s), *args, None, ctypes.c_size_t(1 << 30), None) == 1
+    assert lib.moe_forward(ctypes.byref(s), A, A, None, A, A, A, A, A, MIS, A, None, None, A,
+                           ctypes.c_size_t(1 << 30), None) == 4
+
+
+def test_workspace_checks(lib):
+    s = _shape(T=64)
+    need = ctypes.c_size_t(0)
+    assert lib.moe_workspace_size(ctypes.byref(s), ctypes.byref(need)) == 0
+    S = 64 * 2
+    r = lambda v: (v + 255) // 256 * 256
+    assert need.value == 4 * r(S * 4) + r(17 * 4) + r(S * 512 * 2) + r(S * 256 * 4)
+    ffn = ctypes.c_size_t(0)
+    assert lib.moe_ffn_workspace_size(ctypes.byref(s), ctypes.byref(ffn)) == 0
+    assert ffn.value == r(S * 512 * 2)
+    st = lib.moe_forward(ctypes.byref(s), A, A, None, A, A, A, A, A, A, A, None, None, A,
+                         ctypes.c_size_t(need.value - 1), None)
+    assert st == 5
+    st = lib.moe_expert_ffn(ctypes.byref(s), A, A, A, A, A, A, A, A, A, A, A, ctypes.c_size_t(ffn.value - 1), None)
+    assert st == 5
+
+
+def test_empty_input_enqueues_nothing(lib):
+    s = _shape(T=0)
+    need = ctypes.c_size_t(0)
+    assert lib.moe_workspace_size(ctypes.byref(s), ctypes.byref(need)) == 0
+    assert lib.moe_route(ctypes.byref(s), A, A, None, A, A, None) == 0
+    assert lib.moe_permute(ctypes.byref(s), A, A, A, A, None) == 0
+    assert lib.moe_combine(ctypes.byref(s), A, A, A, A, None) == 0
+    assert lib.moe_forward(ctypes.byref(s), A, A, None, A, A, A, A, A, A, A, None, None, A,
+                           ctypes.c_size_t(need.value), None) == 0
+
+
+def test_quantize_validation(lib):
+    assert lib.moe_quantize_rows(4, 100, 1, A, 1, A, A, None) == 2      # cols % 16
+    assert lib.moe_quantize_rows(-1, 64, 1, A, 1, A, A, None) == 2
+    assert lib.moe_quantize_rows(4, 64, 7, A, 1, A, A, None) == 3
+    assert lib.moe_quantize_rows(4, 64, 1, A, 1, None, A, None) == 1
+    assert lib.moe_quantize_rows(4, 64, 1, MIS, 1, A, A, None) == 4
+    assert lib.moe_quantize_rows(0, 64, 1, A, 1, A, A, None) == 0

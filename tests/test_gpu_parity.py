@@ -1,0 +1,238 @@
+"""GPU parity at oracle-sized shapes: every C-ABI call against the oracle.
+
+Shapes span several tiles of both expert-FFN schedules and have ragged tails
+(token counts and per-expert row counts that are not tile multiples). Inputs
+are drawn by workloads.py or numpy; expected values come from the oracle only.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from int8_weight_moe_amd import (MoeError, moe_combine, moe_expert_ffn, moe_forward, moe_permute,
+                                 moe_quantize_rows, moe_route)
+from int8_weight_moe_amd._lib import MOE_PATH_AUTO, MOE_PATH_STREAM, MOE_PATH_TILED
+from oracle import moe as omoe
+from oracle import quant as oquant
+from tests.helpers import (assert_close_to_oracle, check_routing, experts_to_device, np64,
+                           quantize_experts_oracle)
+
+pytestmark = pytest.mark.gpu
+
+PATHS = [MOE_PATH_STREAM, MOE_PATH_TILED]
+TDT = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+def _case(T, d, f, E, K, act="bf16", scale="bf16", bias=None, seed=0, wscale=0.02):
+    w = workloads.Workload("case", T=T, d=d, f=f, E=E, K=K, act=act, scale=scale,
+                           weight_src="f32" if act == "f32" else "bf16", seed=seed)
+    x = workloads.draw_activations(w)
+    wr, _ = workloads.draw_router(w)
+    src = workloads.draw_expert_weights(w, "cpu")
+    W = quantize_experts_oracle(src, scale)
+    b = None if bias is None else torch.tensor(bias, dtype=torch.float32)
+    return w, x, wr, b, W
+
+
+# --------------------------------------------------------------------------- quantizer
+@pytest.mark.parametrize("src,scale", [("f32", "f32"), ("f32", "bf16"), ("bf16", "bf16"), ("bf16", "f32")])
+def test_quantize_rows_bit_exact(src, scale):
+    rng = np.random.default_rng(0)
+    w = rng.standard_normal((3, 37, 320)).astype(np.float32) * np.float32(0.02)
+    w[0, 3] = 0.0                                   # zero row
+    w[1, 5] = np.round(w[1, 5] * 2 ** 14) / 2 ** 14  # coarse grid -> ties
+    w[2, 7, :] = np.arange(320) * 2.0 ** -7 - 1.0    # dyadic row, exact ties at scale 2^-7 multiples
+    wt = torch.from_numpy(w).to(TDT[src])
+    q, s = moe_quantize_rows(wt.cuda(), TDT[scale])
+    torch.cuda.synchronize()
+    qr, sr = oquant.quantize_rows(np64(wt), scale)
+    assert np.array_equal(q.cpu().numpy(), qr)
+    assert np.array_equal(np64(s), sr)
+
+
+# --------------------------------------------------------------------------- router
+@pytest.mark.parametrize("T,d,E,K,act,bias", [
+    (64, 256, 16, 2, "f32", None),          # tiny workload shape
+    (1, 512, 16, 2, "bf16", None),
+    (77, 1024, 16, 2, "bf16", "hot"),
+    (300, 256, 4, 1, "bf16", None),
+    (50, 192, 40, 3, "f32", "hot"),
+    (33, 128, 64, 8, "bf16", None),
+    (20, 64, 1, 1, "bf16", None),
+])
+def test_route_matches_oracle(T, d, E, K, act, bias):
+    w = workloads.Workload("r", T=T, d=d, f=64, E=E, K=K, act=act, seed=3)
+    x = workloads.draw_activations(w)
+    wr, _ = workloads.draw_router(w)
+    b = None
+    if bias == "hot":
+        b = torch.zeros(E, dtype=torch.float32)
+        b[0] = 2.0
+        if E > 1:
+            b[1] = 2.0
+    ids, gw = moe_route(x.cuda(), wr.cuda(), None if b is None else b.cuda(), K)
+    torch.cuda.synchronize()
+    logits = omoe.router_logits(np64(x), np64(wr), None if b is None else np64(b))
+    check_routing(ids.cpu().numpy(), gw.cpu().numpy(), logits, K)
+
+
+def test_route_exact_ties_go_to_lower_index():
+    T, d, E = 16, 128, 8
+    x = torch.randn(T, d, generator=torch.Generator().manual_seed(1)).to(torch.bfloat16)
+    wr = torch.randn(E, d, generator=torch.Generator().manual_seed(2)).to(torch.bfloat16) * 0.05
+    wr[5] = wr[2]          # experts 2 and 5 have identical logits
+    wr[6] = wr[2]
+    b = torch.zeros(E)
+    b[2] = b[5] = b[6] = 50.0   # ... and they are the top three
+    ids, gw = moe_route(x.cuda(), wr.cuda(), b.cuda(), 2)
+    torch.cuda.synchronize()
+    assert ids.cpu().tolist() == [[2, 5]] * T
+    assert torch.all(gw.cpu() == 0.5)
+
+
+# --------------------------------------------------------------------------- permute
+@pytest.mark.parametrize("T,K,E,kind", [
+    (1, 2, 16, "rand"), (64, 2, 16, "rand"), (1000, 2, 16, "hot"), (4096, 2, 16, "one"),
+    (333, 3, 5, "rand"), (16384, 2, 16, "hot"), (70, 1, 64, "rand"), (7, 8, 8, "perm"),
+])
+def test_permute_bit_exact(T, K, E, kind):
+    rng = np.random.default_rng(T + K + E)
+    if kind == "rand":
+        ids = rng.integers(0, E, size=(T, K))
+    elif kind == "hot":
+        ids = np.where(rng.random((T, K)) < 0.4, rng.integers(0, 2, size=(T, K)), rng.integers(0, E, size=(T, K)))
+    elif kind == "one":
+        ids = np.full((T, K), E - 1)
+    else:
+        ids = np.stack([rng.permutation(E)[:K] for _ in range(T)])
+    ids = ids.astype(np.int32)
+    off, ss, s2r = moe_permute(torch.from_numpy(ids).cuda(), E)
+    torch.cuda.synchronize()
+    ro, rs, rr = omoe.permute(ids, E)
+    assert np.array_equal(off.cpu().numpy(), ro)
+    assert np.array_equal(ss.cpu().numpy(), rs)
+    assert np.array_equal(s2r.cpu().numpy(), rr)
+
+
+def test_permute_out_of_range_ids_are_not_placed():
+    ids = np.array([[0, 3], [16, 1], [2, -1]], dtype=np.int32)
+    off, ss, s2r = moe_permute(torch.from_numpy(ids).cuda(), 16)
+    torch.cuda.synchronize()
+    s2r = s2r.cpu().numpy()
+    assert off.cpu().numpy()[-1] == 4
+    assert s2r[2] == -1 and s2r[5] == -1
+    assert ss.cpu().numpy()[4:].tolist() == [-1, -1]
+    valid = [0, 1, 3, 4]
+    assert sorted(s2r[valid].tolist()) == [0, 1, 2, 3]
+
+
+# --------------------------------------------------------------------------- expert FFN
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("T,d,f,E,K,act,scale,routing", [
+    (64, 256, 512, 16, 2, "f32", "f32", "router"),     # the tiny workload
+    (200, 384, 640, 16, 2, "bf16", "bf16", "router"),  # ragged rows per expert
+    (600, 256, 384, 4, 2, "bf16", "bf16", "skew"),     # several row tiles per expert, ragged tail
+    (9, 128, 192, 16, 2, "bf16", "bf16", "router"),    # most experts empty
+    (150, 192, 256, 8, 1, "bf16", "f32", "one"),        # every row on one expert
+])
+def test_expert_ffn_matches_oracle(path, T, d, f, E, K, act, scale, routing):
+    w, x, wr, _, W = _case(T, d, f, E, K, act, scale, seed=7)
+    rng = np.random.default_rng(11)
+    if routing == "router":
+        ids, _ = omoe.topk_gate(omoe.router_logits(np64(x), np64(wr)), K)
+    elif routing == "skew":
+        ids = np.stack([rng.choice(E, size=K, replace=False, p=[0.55, 0.25, 0.15, 0.05]) for _ in range(T)])
+    else:
+        ids = np.zeros((T, K), dtype=np.int32) + 3
+    ids = ids.astype(np.int32)
+    off, ss, s2r = omoe.permute(ids, E)
+    ex = experts_to_device(W, TDT[scale])
+    y_rows = moe_expert_ffn(x.cuda(), torch.from_numpy(off).cuda(), torch.from_numpy(ss).cuda(), ex, K, path=path)
+    torch.cuda.synchronize()
+    o = omoe.expert_outputs(np64(x), ids, W)               # [T, K, d] per slot
+    ref_rows = o.reshape(T * K, -1)[ss]                    # sorted-row order
+    assert_close_to_oracle(np64(y_rows), ref_rows, "y_rows")
+
+
+# --------------------------------------------------------------------------- combine
+@pytest.mark.parametrize("T,d,K,act", [(1, 64, 2, "bf16"), (129, 320, 2, "f32"), (40, 128, 5, "bf16")])
+def test_combine_matches_oracle(T, d, K, act):
+    rng = np.random.default_rng(5)
+    E = 8
+    ids = np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int32)
+    off, ss, s2r = omoe.permute(ids, E)
+    rows = rng.standard_normal((T * K, d)).astype(np.float32)
+    gw = rng.random((T, K)).astype(np.float32)
+    gw /= gw.sum(axis=1, keepdims=True)
+    y = moe_combine(torch.from_numpy(rows).cuda(), torch.from_numpy(s2r).cuda(), torch.from_numpy(gw).cuda(),
+                    TDT[act])
+    torch.cuda.synchronize()
+    o = rows.astype(np.float64)[s2r].reshape(T, K, d)
+    ref = omoe.combine(o, gw)
+    got = np64(y)
+    # fp32 accumulation of K terms, then the output rounding of the dtype
+    rel = 2.0 ** -8 if act == "bf16" else 1e-6
+    assert np.all(np.abs(got - ref) <= rel * np.abs(ref) + 1e-6 * np.abs(ref).max())
+
+
+# --------------------------------------------------------------------------- whole layer
+@pytest.mark.parametrize("path", [MOE_PATH_AUTO, MOE_PATH_STREAM, MOE_PATH_TILED])
+@pytest.mark.parametrize("T,d,f,E,K,act,scale,bias", [
+    (64, 256, 512, 16, 2, "f32", "f32", None),       # tiny workload
+    (1, 256, 512, 16, 2, "bf16", "bf16", None),      # a single token
+    (257, 256, 320, 16, 2, "bf16", "bf16", [2.0, 2.0] + [0.0] * 14),  # skewed router, ragged
+    (40, 128, 192, 8, 8, "bf16", "bf16", None),      # K = E: dense mixture
+    (33, 192, 256, 1, 1, "bf16", "bf16", None),      # E = K = 1: dense int8 MLP
+    (100, 128, 128, 16, 2, "bf16", "bf16", [0.0] * 5 + [100.0] + [0.0] * 10),  # hot expert 5 in every token
+])
+def test_forward_matches_oracle(path, T, d, f, E, K, act, scale, bias):
+    w, x, wr, b, W = _case(T, d, f, E, K, act, scale, bias=bias, seed=9)
+    ex = experts_to_device(W, TDT[scale])
+    y, ids, gw = moe_forward(x.cuda(), wr.cuda(), None if b is None else b.cuda(), ex, K, path=path)
+    torch.cuda.synchronize()
+    x64, wr64 = np64(x), np64(wr)
+    b64 = None if b is None else np64(b)
+    logits = omoe.router_logits(x64, wr64, b64)
+    ids_g = ids.cpu().numpy()
+    check_routing(ids_g, gw.cpu().numpy(), logits, K)
+    ref = omoe.moe_forward(x64, wr64, b64, W, K, ids=ids_g)["y"]
+    assert_close_to_oracle(np64(y), ref, "y")
+    if K == E:
+        assert_close_to_oracle(np64(y), omoe.dense_mixture(x64, wr64, b64, W), "y vs dense mixture")
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_forward_equals_staged_calls_bitwise(path):
+    w, x, wr, b, W = _case(300, 256, 384, 16, 2, "bf16", "bf16", bias=[1.0] + [0.0] * 15, seed=4)
+    ex = experts_to_device(W, torch.bfloat16)
+    xg, wrg, bg = x.cuda(), wr.cuda(), b.cuda()
+    y, ids, gw = moe_forward(xg, wrg, bg, ex, 2, path=path)
+    ids2, gw2 = moe_route(xg, wrg, bg, 2)
+    off, ss, s2r = moe_permute(ids2, 16)
+    rows = moe_expert_ffn(xg, off, ss, ex, 2, path=path)
+    y2 = moe_combine(rows, s2r, gw2, torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(ids, ids2) and torch.equal(gw, gw2)
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_forward_deterministic_and_token_permutation_equivariant(path):
+    w, x, wr, b, W = _case(192, 256, 256, 16, 2, "bf16", "bf16", seed=6)
+    ex = experts_to_device(W, torch.bfloat16)
+    xg, wrg = x.cuda(), wr.cuda()
+    y1, i1, g1 = moe_forward(xg, wrg, None, ex, 2, path=path)
+    y2, i2, g2 = moe_forward(xg, wrg, None, ex, 2, path=path)
+    perm = torch.from_numpy(np.random.default_rng(0).permutation(192)).cuda()
+    y3, i3, g3 = moe_forward(xg[perm].contiguous(), wrg, None, ex, 2, path=path)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    assert torch.equal(i3, i1[perm]) and torch.equal(g3, g1[perm])
+    assert torch.equal(y3.view(torch.int16), y1[perm].view(torch.int16))
+
+
+def test_library_errors_raise():
+    x = torch.zeros((4, 100), dtype=torch.bfloat16, device="cuda")   # d not a multiple of 64
+    wr = torch.zeros((16, 100), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(MoeError):
+        moe_route(x, wr, None, 2)
