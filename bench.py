@@ -48,6 +48,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-experts", type=int, default=4)
     ap.add_argument("--path", choices=["auto", "stream", "tiled"], default="auto")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (reference for HBM byte counters)")
     return ap.parse_args()
 
 
@@ -337,6 +339,16 @@ def main():
             }
             layer.bias = orig_bias
             del xp
+
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib << 20
+        a = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        log(f"copy calibration: 3 x {args.copy_calibration_mib} MiB device copies")
+        del a, b
 
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
