@@ -34,8 +34,10 @@
  *     available from moe_last_error() on the calling thread. A launch failure
  *     reported by HIP maps to MOE_ERR_HIP. Device-side faults surface at the
  *     caller's next synchronisation.
- *   - Weight layout is (out, in): w_gate, w_up [E, f, d]; w_down [E, d, f];
- *     router_w [E, d]; scales s_gate, s_up [E, f], s_down [E, d].
+ *   - Expert weights are (out, in) matrices w_gate, w_up [E, f, d] and
+ *     w_down [E, d, f], held by the FFN calls in the TILED INT8 LAYOUT that
+ *     moe_pack_rows produces (see there). router_w [E, d] is row-major;
+ *     scales s_gate, s_up [E, f], s_down [E, d] are row-major.
  *   - Slots: token t's k-th choice is slot s = t*K + k.
  *   - T = 0 is valid and enqueues nothing.
  */
@@ -82,7 +84,7 @@ typedef struct moe_shape {
 } moe_shape;
 
 /* ABI version of this header (bumped on any signature change). */
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 int32_t moe_abi_version(void);
 
 /* Static description of a status code. */
@@ -123,7 +125,7 @@ moe_status moe_permute(const moe_shape* shape, const int32_t* topk_ids,
 /* Expert SwiGLU FFNs on the permuted rows (the ExpertsInt8 contraction).
  *   x              [T, d] act_dtype (row of sorted row r is token sorted_slots[r] / K)
  *   expert_offsets [E+1], sorted_slots [T*K] from moe_permute
- *   w_gate, w_up   [E, f, d] int8;  w_down [E, d, f] int8
+ *   w_gate, w_up   [E, f, d] int8;  w_down [E, d, f] int8 -- tiled layout (moe_pack_rows)
  *   s_gate, s_up   [E, f] scale_dtype;  s_down [E, d] scale_dtype
  *   y_rows         [T*K, d] fp32 out: row r = output of sorted row r's expert
  *   workspace      >= moe_ffn_workspace_size bytes (holds h)
@@ -174,6 +176,17 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const void* router
  * unspecified codes. Bit-exact (the rounding decisions are exact). */
 moe_status moe_quantize_rows(int64_t rows, int32_t cols, int32_t src_dtype, const void* w,
                              int32_t scale_dtype, int8_t* q, void* s, hipStream_t stream);
+
+/* Tiled int8 layout of the expert weights (load time, next to the quantizer).
+ * The kernels read a wavefront's MFMA operands as whole 1 KiB blocks: a
+ * row-major int8 matrix q [rows, cols] (rows % 16 == 0, cols % 64 == 0) is
+ * stored as blocks of 16 rows x 64 columns; block (rg, ks) covers rows
+ * 16*rg..+16 and columns 64*ks..+64 and sits at block index rg*(cols/64) + ks;
+ * inside it, element (r, c) is byte 256*(c/16) + 16*r + (c%16). An expert
+ * tensor [E, out, in] is packed as rows = E*out, cols = in.
+ *   q [rows, cols] int8 row-major in, packed [rows*cols] int8 out (not in place).
+ * A byte permutation: bit-exact. */
+moe_status moe_pack_rows(int64_t rows, int32_t cols, const int8_t* q, int8_t* packed, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -11,6 +11,7 @@ import os
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libmoe_int8.so")
 
+ABI_VERSION = 2
 MOE_OK = 0
 STATUS_NAMES = {
     0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_DTYPE", 4: "MOE_ERR_ALIGN",
@@ -23,6 +24,7 @@ MOE_PATH_AUTO, MOE_PATH_STREAM, MOE_PATH_TILED = 0, 1, 2
 EXPORTS = (
     "moe_abi_version", "moe_status_str", "moe_last_error", "moe_workspace_size", "moe_ffn_workspace_size",
     "moe_route", "moe_permute", "moe_expert_ffn", "moe_expert_gate_up", "moe_expert_down", "moe_combine", "moe_forward", "moe_quantize_rows",
+    "moe_pack_rows",
 )
 
 
@@ -54,6 +56,7 @@ _SIGS = {
     "moe_combine": (ctypes.c_int32, [_SHAPE, _P, _P, _P, _P, _P]),
     "moe_forward": (ctypes.c_int32, [_SHAPE, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "moe_quantize_rows": (ctypes.c_int32, [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_int32, _P, _P, _P]),
+    "moe_pack_rows": (ctypes.c_int32, [ctypes.c_int64, ctypes.c_int32, _P, _P, _P]),
 }
 
 _lib = None
@@ -73,8 +76,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         fn = getattr(lib, name)
         fn.restype = res
         fn.argtypes = args
-    if lib.moe_abi_version() != 1:
-        raise ImportError(f"libmoe_int8 ABI version {lib.moe_abi_version()} != 1")
+    if lib.moe_abi_version() != ABI_VERSION:
+        raise ImportError(f"libmoe_int8 ABI version {lib.moe_abi_version()} != {ABI_VERSION}")
     _lib = lib
     return lib
 

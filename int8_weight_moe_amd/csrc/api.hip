@@ -330,4 +330,17 @@ moe_status moe_quantize_rows(int64_t rows, int32_t cols, int32_t src_dtype, cons
   return MOE_OK;
 }
 
+moe_status moe_pack_rows(int64_t rows, int32_t cols, const int8_t* q, int8_t* packed, hipStream_t stream) {
+  if (rows < 0 || rows % 16) return fail(MOE_ERR_SHAPE, "rows=%ld must be a non-negative multiple of 16", (long)rows);
+  if (cols < 64 || cols > (1 << 20) || cols % 64) return fail(MOE_ERR_SHAPE, "cols=%d must be a multiple of 64 in [64, 2^20]", cols);
+  if (rows * (int64_t)cols / 16 > 0x7fffffffL * 256L) return fail(MOE_ERR_SHAPE, "matrix too large");
+  REQUIRE_PTR(q);
+  REQUIRE_PTR(packed);
+  if (q == packed) return fail(MOE_ERR_UNSUPPORTED, "packing cannot be done in place");
+  if (rows == 0) return MOE_OK;
+  const hipError_t e = moe::launch_pack_rows(rows, cols, q, packed, stream);
+  if (e != hipSuccess) return hip_fail(e, "pack launch");
+  return MOE_OK;
+}
+
 }  // extern "C"

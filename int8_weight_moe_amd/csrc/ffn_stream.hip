@@ -5,9 +5,11 @@
 // I/O-bound, and ExpertsInt8 moves the weights from HBM at half the bytes of
 // BF16). Each wave owns one (expert, group of 16*NG output channels) item and
 // runs the full reduction for all of the expert's rows (up to 16*RB per pass):
-//   - the weight rows of its channels stream from HBM in 64-byte pieces per
-//     channel and step (lane l: channel l%16, bytes 16*(l/16)..+16), with the
-//     loads of the next P-1 steps in flight;
+//   - weights are in the tiled layout (pack.hip), so each 16-channel group
+//     is one contiguous run of 1 KiB blocks; per 64-wide step a wave reads one
+//     block per group and matrix (lane l: channel l%16, bytes 16*(l/16)..+16)
+//     with non-temporal loads, and the loads of the next P-1 steps are in
+//     flight;
 //   - the int8 codes become bf16 in registers (exact) and feed 16x16x32 bf16
 //     MFMA, with the channels as MFMA rows and the tokens as MFMA columns;
 //   - a 64-wide step is two MFMAs: code bytes 0-7 of each lane pair with
@@ -24,7 +26,30 @@ namespace moe {
 
 namespace {
 
-constexpr int kStreamWaves = 4;
+// Schedule parameters (compile-time; overridable for tuning builds):
+// NG 16-channel groups per wave, RB 16-row blocks per pass, P-stage load ring,
+// WAVES waves per workgroup. Measured on MI355X: the gate/up pass (two
+// matrices per group) streams best with one group per wave, the down pass
+// with four groups and a four-deep ring.
+#ifndef MOE_STREAM_NG_GU
+#define MOE_STREAM_NG_GU 1
+#endif
+#ifndef MOE_STREAM_P_GU
+#define MOE_STREAM_P_GU 3
+#endif
+#ifndef MOE_STREAM_NG_DN
+#define MOE_STREAM_NG_DN 4
+#endif
+#ifndef MOE_STREAM_P_DN
+#define MOE_STREAM_P_DN 4
+#endif
+#ifndef MOE_STREAM_RB
+#define MOE_STREAM_RB 2
+#endif
+#ifndef MOE_STREAM_WAVES
+#define MOE_STREAM_WAVES 4
+#endif
+constexpr int kStreamWaves = MOE_STREAM_WAVES;
 
 template <bool kGateUp, typename Act, bool kScaleBf16, int NG, int RB, int P>
 __global__ __launch_bounds__(kStreamWaves * kWave) void ffn_stream_kernel(
@@ -62,12 +87,14 @@ __global__ __launch_bounds__(kStreamWaves * kWave) void ffn_stream_kernel(
   if (e < 0) return;
 
   const int ch_base = grp * 16 * NG;
+  // first 1 KiB block of each 16-channel group (tiled layout), this lane's piece
   const int8_t* wp[NG][NMAT];
 #pragma unroll
   for (int ng = 0; ng < NG; ++ng) {
-    const long ch = (long)e * N + ch_base + ng * 16 + li;
-    wp[ng][0] = W0 + ch * Kd + 16 * lg;
-    if constexpr (kGateUp) wp[ng][1] = W1 + ch * Kd + 16 * lg;
+    const long group = ((long)e * N + ch_base + ng * 16) >> 4;
+    const long off = group * (long)(Kd >> 6) * 1024 + 16 * lane;
+    wp[ng][0] = W0 + off;
+    if constexpr (kGateUp) wp[ng][1] = W1 + off;
   }
   // per-lane scales of the 4 channels this lane holds in the result
   float sc[NG][NMAT][4];
@@ -120,7 +147,7 @@ __global__ __launch_bounds__(kStreamWaves * kWave) void ffn_stream_kernel(
 #pragma unroll
       for (int ng = 0; ng < NG; ++ng)
 #pragma unroll
-        for (int m = 0; m < NMAT; ++m) b[ng][m] = *reinterpret_cast<const uint4*>(wp[ng][m] + off);
+        for (int m = 0; m < NMAT; ++m) b[ng][m] = load_nt16(wp[ng][m] + (long)s * 1024);
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
         if (rb < nrb && aok[rb]) {
@@ -196,7 +223,9 @@ __global__ __launch_bounds__(kStreamWaves * kWave) void ffn_stream_kernel(
 
 template <bool kGateUp, typename Act, bool kScaleBf16>
 hipError_t launch_stream_pass(const FfnArgs& a, hipStream_t stream) {
-  constexpr int NG = 2, RB = 2, P = 3;
+  constexpr int NG = kGateUp ? MOE_STREAM_NG_GU : MOE_STREAM_NG_DN;
+  constexpr int P = kGateUp ? MOE_STREAM_P_GU : MOE_STREAM_P_DN;
+  constexpr int RB = MOE_STREAM_RB;
   const int N = kGateUp ? a.f : a.d;
   const int Kd = kGateUp ? a.d : a.f;
   const int gpe = N / (16 * NG);

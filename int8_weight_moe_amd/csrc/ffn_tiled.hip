@@ -18,10 +18,12 @@
 // Waves are arranged WM x WN; a wave owns (BM/WM) x (BN/WN) outputs and issues
 // 16x16x32 bf16 MFMAs with the channels as MFMA rows and the tokens as MFMA
 // columns, so each lane ends with 4 consecutive channels of one row.
-// Tiles are numbered expert by expert, row tile major, channel tile minor;
-// workgroup ids are spread so that each XCD (workgroups are dealt round-robin
-// to the 8 XCDs) runs a contiguous range of tiles and shares their operands in
-// its own L2.
+// Tile order: row tiles are numbered expert by expert; tiles are visited in
+// groups of GM consecutive row tiles, channel tile by channel tile inside a
+// group, so the tiles that run together share GM activation tiles and a few
+// weight tiles. Workgroup ids are spread so that each XCD (workgroups are dealt
+// round-robin to the 8 XCDs) runs a contiguous range of that order and keeps
+// its operands in its own L2.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -33,16 +35,33 @@ constexpr int kBK = 64;      // reduction step (elements)
 constexpr int kChunks = kBK / 8;  // 16-byte bf16 chunks per LDS row
 constexpr int kXcds = 8;
 
+// Tile shape (compile-time; overridable for tuning builds).
+#ifndef MOE_TILE_BM
+#define MOE_TILE_BM 256
+#endif
+#ifndef MOE_TILE_BN
+#define MOE_TILE_BN 256
+#endif
+#ifndef MOE_TILE_WM
+#define MOE_TILE_WM 4
+#endif
+#ifndef MOE_TILE_WN
+#define MOE_TILE_WN 2
+#endif
+#ifndef MOE_TILE_GM
+#define MOE_TILE_GM 4
+#endif
+
 __device__ __forceinline__ int swz(int row, int chunk) {
   return row * kBK + ((chunk ^ (row & 7)) << 3);
 }
 
-template <bool kGateUp, typename Act, bool kScaleBf16, int BM, int BN, int WM, int WN>
+template <bool kGateUp, typename Act, bool kScaleBf16, int BM, int BN, int WM, int WN, int GM>
 __global__ __launch_bounds__(WM * WN * kWave) void ffn_tiled_kernel(
     const Act* __restrict__ X, const int32_t* __restrict__ sorted_slots, int topk,
     const int8_t* __restrict__ W0, const int8_t* __restrict__ W1, const void* __restrict__ S0,
     const void* __restrict__ S1, const int32_t* __restrict__ offsets, int E, int N, int Kd, int n_tiles_n,
-    int total_blocks, void* __restrict__ out) {
+    int m_tiles, int total_blocks, void* __restrict__ out) {
   constexpr int NT = WM * WN * kWave;       // threads
   constexpr int TM = BM / WM;               // rows per wave
   constexpr int TN = BN / WN;               // effective columns per wave
@@ -69,8 +88,14 @@ __global__ __launch_bounds__(WM * WN * kWave) void ffn_tiled_kernel(
   // ---- XCD-contiguous tile id, then (expert, row tile, channel tile)
   const int per_xcd = total_blocks / kXcds;
   const int tile = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
-  const int mt_global = tile / n_tiles_n;
-  const int nt = tile - mt_global * n_tiles_n;
+  const int group_tiles = GM * n_tiles_n;
+  const int group = tile / group_tiles;
+  const int in_group = tile - group * group_tiles;
+  const int gm = min(GM, m_tiles - group * GM);   // row tiles in this (possibly last) group
+  if (gm <= 0) return;
+  const int mt_global = group * GM + in_group % gm;
+  const int nt = in_group / gm;
+  if (nt >= n_tiles_n) return;
   int e = -1, row0 = 0, nrows = 0;
   {
     int cum = 0;
@@ -108,25 +133,29 @@ __global__ __launch_bounds__(WM * WN * kWave) void ffn_tiled_kernel(
     }
     a_src[i] = X + src + ck * 8;
   }
-  // channels past N (last channel tile when N is not a tile multiple) load zeros
+  // Weight pieces: the tile's channels are BN/16 groups of 16, each one 1 KiB
+  // block per step in the tiled layout; piece c = 64*j + l is lane l's 16 bytes
+  // of block j (tile row 16*j + l%16, reduction bytes 16*(l/16)..+16).
+  // Channels past N (last channel tile when N is not a tile multiple) load zeros.
   const int8_t* b_src[B_PIECES];
   bool b_ok[B_PIECES];
 #pragma unroll
   for (int i = 0; i < B_PIECES; ++i) {
     const int c = tid + i * NT;
-    const int r = c / (kBK / 16);
-    const int pc = c % (kBK / 16);
+    const int j = c >> 6;
+    const int l = c & 63;
     const int8_t* base;
     int chl;
     if constexpr (kGateUp) {
-      base = (r < BN / 2) ? W0 : W1;
-      chl = n0 + (r % (BN / 2));
+      base = (j < BN / 32) ? W0 : W1;
+      chl = n0 + 16 * (j % (BN / 32));
     } else {
       base = W0;
-      chl = n0 + r;
+      chl = n0 + 16 * j;
     }
     b_ok[i] = chl < N;
-    b_src[i] = base + ((long)e * N + (b_ok[i] ? chl : 0)) * Kd + pc * 16;
+    const long group = ((long)e * N + (b_ok[i] ? chl : 0)) >> 4;
+    b_src[i] = base + group * (long)(Kd / kBK) * 1024 + 16 * l;
   }
 
   // ---- register staging of one step
@@ -149,7 +178,7 @@ __global__ __launch_bounds__(WM * WN * kWave) void ffn_tiled_kernel(
     }
 #pragma unroll
     for (int i = 0; i < B_PIECES; ++i)
-      b_reg[i] = b_ok[i] ? *reinterpret_cast<const uint4*>(b_src[i] + off) : make_uint4(0, 0, 0, 0);
+      b_reg[i] = b_ok[i] ? load_nt16(b_src[i] + (long)kt * 1024) : make_uint4(0, 0, 0, 0);
   };
   auto lstore = [&](int buf) {
 #pragma unroll
@@ -160,8 +189,8 @@ __global__ __launch_bounds__(WM * WN * kWave) void ffn_tiled_kernel(
 #pragma unroll
     for (int i = 0; i < B_PIECES; ++i) {
       const int c = tid + i * NT;
-      const int r = c / (kBK / 16);
-      const int pc = c % (kBK / 16);
+      const int r = 16 * (c >> 6) + (c & 15);
+      const int pc = (c & 63) >> 4;
       const bf16x8 lo = i8x8_to_bf16(b_reg[i].x, b_reg[i].y);
       const bf16x8 hi = i8x8_to_bf16(b_reg[i].z, b_reg[i].w);
       *reinterpret_cast<bf16x8*>(&Bs[buf][swz(r, 2 * pc)]) = lo;
@@ -251,24 +280,25 @@ __global__ __launch_bounds__(WM * WN * kWave) void ffn_tiled_kernel(
 
 template <bool kGateUp, typename Act, bool kScaleBf16>
 hipError_t launch_tiled_pass(const FfnArgs& a, hipStream_t stream) {
-  constexpr int BM = 128, BN = 128, WM = 2, WN = 2;
+  constexpr int BM = MOE_TILE_BM, BN = MOE_TILE_BN, WM = MOE_TILE_WM, WN = MOE_TILE_WN, GM = MOE_TILE_GM;
   constexpr int CH_TILE = kGateUp ? BN / 2 : BN;
   const int N = kGateUp ? a.f : a.d;
   const int Kd = kGateUp ? a.d : a.f;
   const int n_tiles_n = (N + CH_TILE - 1) / CH_TILE;
+  // row tiles: at most one partial tile per expert beyond S / BM
   const long m_tiles_max = (long)(a.S + BM - 1) / BM + a.E;
   long blocks = m_tiles_max * n_tiles_n;
   blocks = (blocks + kXcds - 1) / kXcds * kXcds;
   const dim3 grid((unsigned)blocks);
   const dim3 block(WM * WN * kWave);
   if constexpr (kGateUp) {
-    hipLaunchKernelGGL((ffn_tiled_kernel<true, Act, kScaleBf16, BM, BN, WM, WN>), grid, block, 0, stream,
+    hipLaunchKernelGGL((ffn_tiled_kernel<true, Act, kScaleBf16, BM, BN, WM, WN, GM>), grid, block, 0, stream,
                        static_cast<const Act*>(a.x), a.sorted_slots, a.K, a.w_gate, a.w_up, a.s_gate, a.s_up,
-                       a.offsets, a.E, N, Kd, n_tiles_n, (int)blocks, static_cast<void*>(a.h));
+                       a.offsets, a.E, N, Kd, n_tiles_n, (int)m_tiles_max, (int)blocks, static_cast<void*>(a.h));
   } else {
-    hipLaunchKernelGGL((ffn_tiled_kernel<false, __bf16, kScaleBf16, BM, BN, WM, WN>), grid, block, 0, stream,
+    hipLaunchKernelGGL((ffn_tiled_kernel<false, __bf16, kScaleBf16, BM, BN, WM, WN, GM>), grid, block, 0, stream,
                        static_cast<const __bf16*>(a.h), a.sorted_slots, a.K, a.w_down, nullptr, a.s_down, nullptr,
-                       a.offsets, a.E, N, Kd, n_tiles_n, (int)blocks, static_cast<void*>(a.y_rows));
+                       a.offsets, a.E, N, Kd, n_tiles_n, (int)m_tiles_max, (int)blocks, static_cast<void*>(a.y_rows));
   }
   return hipGetLastError();
 }

@@ -21,9 +21,9 @@ struct FfnArgs {
   bool scale_bf16;            // scale dtype
   const int32_t* offsets;     // [E + 1]
   const int32_t* sorted_slots;  // [S]
-  const int8_t* w_gate;       // [E, f, d]
-  const int8_t* w_up;         // [E, f, d]
-  const int8_t* w_down;       // [E, d, f]
+  const int8_t* w_gate;       // [E, f, d], tiled int8 layout
+  const int8_t* w_up;         // [E, f, d], tiled int8 layout
+  const int8_t* w_down;       // [E, d, f], tiled int8 layout
   const void* s_gate;         // [E, f]
   const void* s_up;           // [E, f]
   const void* s_down;         // [E, d]
@@ -42,6 +42,8 @@ hipError_t launch_tiled_down(const FfnArgs& a, hipStream_t stream);
 
 hipError_t launch_combine(const float* y_rows, const int32_t* slot_to_row, const float* topk_w, int T, int d,
                           int K, bool act_bf16, void* y, hipStream_t stream);
+
+hipError_t launch_pack_rows(long rows, int cols, const int8_t* src, int8_t* dst, hipStream_t stream);
 
 hipError_t launch_quantize_rows(int64_t rows, int cols, bool src_bf16, const void* w, bool scale_bf16, int8_t* q,
                                 void* s, hipStream_t stream);

@@ -1,12 +1,13 @@
 // Router and top-K gate (Jamba-1.5 paper, "Model Architecture": a router picks
 // the top K of n experts for every token).
 //
-// One workgroup scores 16 tokens against every expert. The 8 waves split the
-// hidden dimension, each accumulating a 16x16 logit tile per block of 16
+// One workgroup scores 16 tokens against every expert. The 16 waves split the
+// hidden dimension (so even a decode batch of a few tokens keeps many waves
+// loading in parallel), each accumulating a 16x16 logit tile per block of 16
 // experts with MFMA (bf16 inputs: 16x16x32 bf16, products exact, fp32 sums;
 // fp32 inputs: 16x16x4 fp32). The partial tiles are summed through LDS in a
 // fixed wave order, so the logits do not depend on scheduling. Then each wave
-// takes two tokens: lane e holds logit e, K rounds of a wavefront argmax
+// takes one token: lane e holds logit e, K rounds of a wavefront argmax
 // (ties to the lower expert index) pick the experts, and the gate weights are
 // the softmax renormalised over the chosen set,
 //   w_k = exp(l_k - l_max) / sum_j exp(l_j - l_max).
@@ -17,7 +18,7 @@ namespace moe {
 
 namespace {
 
-constexpr int kRouterWaves = 8;
+constexpr int kRouterWaves = 16;
 constexpr int kRouterTokens = 16;
 constexpr int kMaxExperts = 64;
 

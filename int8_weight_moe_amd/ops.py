@@ -23,8 +23,9 @@ _DT = {torch.float32: MOE_F32, torch.bfloat16: MOE_BF16}
 class Int8Experts:
     """ExpertsInt8 weights of one MoE layer: int8 codes plus per-output-channel scales.
 
-    q_gate, q_up [E, f, d] int8; q_down [E, d, f] int8; s_gate, s_up [E, f]; s_down [E, d]
-    (scales all fp32 or all bf16).
+    q_gate, q_up [E, f, d] int8; q_down [E, d, f] int8, each holding its codes in
+    the tiled layout of moe_pack_rows (the tensor shape is kept for the sizes);
+    s_gate, s_up [E, f]; s_down [E, d] (scales all fp32 or all bf16).
     """
     q_gate: torch.Tensor
     q_up: torch.Tensor
@@ -239,10 +240,30 @@ def moe_quantize_rows(w: torch.Tensor, scale_dtype: torch.dtype):
     return q, s
 
 
+def moe_pack_rows(q: torch.Tensor) -> torch.Tensor:
+    """Row-major int8 codes [..., rows, cols] -> the tiled layout (same shape, permuted bytes)."""
+    lib = _lib_handle()
+    cols = q.shape[-1]
+    rows = q.numel() // cols
+    out = torch.empty_like(q)
+    _lib.check(lib.moe_pack_rows(ctypes.c_int64(rows), ctypes.c_int32(cols), _ptr(q), _ptr(out), _stream()))
+    return out
+
+
+def pack_experts(q_gate: torch.Tensor, q_up: torch.Tensor, q_down: torch.Tensor, s_gate: torch.Tensor,
+                 s_up: torch.Tensor, s_down: torch.Tensor) -> Int8Experts:
+    """Row-major int8 codes + scales -> Int8Experts in the kernels' tiled layout."""
+    return Int8Experts(moe_pack_rows(q_gate), moe_pack_rows(q_up), moe_pack_rows(q_down), s_gate, s_up, s_down)
+
+
 def quantize_experts(w_gate: torch.Tensor, w_up: torch.Tensor, w_down: torch.Tensor,
                      scale_dtype: torch.dtype) -> Int8Experts:
-    """Quantize a layer's unquantized (out, in) expert weights with moe_quantize_rows."""
-    qg, sg = moe_quantize_rows(w_gate, scale_dtype)
-    qu, su = moe_quantize_rows(w_up, scale_dtype)
-    qd, sd = moe_quantize_rows(w_down, scale_dtype)
-    return Int8Experts(qg, qu, qd, sg, su, sd)
+    """Load-time ExpertsInt8: quantize the (out, in) expert weights, then tile the codes."""
+    out = []
+    scales = []
+    for w in (w_gate, w_up, w_down):
+        q, s = moe_quantize_rows(w, scale_dtype)
+        out.append(moe_pack_rows(q))
+        scales.append(s)
+        del q
+    return Int8Experts(out[0], out[1], out[2], scales[0], scales[1], scales[2])

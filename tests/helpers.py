@@ -43,12 +43,34 @@ def quantize_experts_oracle(src: dict, scale: str) -> dict:
 
 
 def experts_to_device(W: dict, scale_dtype: torch.dtype, device="cuda"):
-    from int8_weight_moe_amd import Int8Experts
+    """Oracle codes and scales -> Int8Experts on the GPU (codes tiled by the library's moe_pack_rows)."""
+    from int8_weight_moe_amd import pack_experts
     t = {}
     for k in ("gate", "up", "down"):
         t["q_" + k] = torch.from_numpy(W["q_" + k]).to(device)
         t["s_" + k] = torch.from_numpy(W["s_" + k]).to(scale_dtype).to(device)
-    return Int8Experts(t["q_gate"], t["q_up"], t["q_down"], t["s_gate"], t["s_up"], t["s_down"])
+    return pack_experts(t["q_gate"], t["q_up"], t["q_down"], t["s_gate"], t["s_up"], t["s_down"])
+
+
+def tiled_to_rowmajor(p: np.ndarray) -> np.ndarray:
+    """Inverse of the tiled int8 layout (include/moe_int8.h, moe_pack_rows): a pure index permutation.
+
+    Tiled byte order per matrix [R, C]: block (rg, ks) of 16 rows x 64 columns at
+    block index rg*(C/64)+ks, element (r, c) at 256*(c/16) + 16*r + c%16 inside it.
+    """
+    shape = p.shape
+    C = shape[-1]
+    R = p.size // C
+    a = p.reshape(R // 16, C // 64, 4, 16, 16)          # [rg, ks, g, r, b]
+    return a.transpose(0, 3, 1, 2, 4).reshape(shape)    # [rg, r, ks, g, b]
+
+
+def rowmajor_to_tiled(q: np.ndarray) -> np.ndarray:
+    shape = q.shape
+    C = shape[-1]
+    R = q.size // C
+    a = q.reshape(R // 16, 16, C // 64, 4, 16)          # [rg, r, ks, g, b]
+    return a.transpose(0, 2, 3, 1, 4).reshape(shape)    # [rg, ks, g, r, b]
 
 
 def check_routing(ids_gpu: np.ndarray, w_gpu: np.ndarray, logits: np.ndarray, K: int):

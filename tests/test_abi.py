@@ -49,7 +49,7 @@ def test_header_constants_match_binding():
 def test_status_strings(lib):
     for st in range(8):
         assert lib.moe_status_str(st)
-    assert lib.moe_abi_version() == 1
+    assert lib.moe_abi_version() == _lib.ABI_VERSION
 
 
 def _shape(**kw):
@@ -118,6 +118,15 @@ def test_empty_input_enqueues_nothing(lib):
     assert lib.moe_combine(ctypes.byref(s), A, A, A, A, None) == 0
     assert lib.moe_forward(ctypes.byref(s), A, A, None, A, A, A, A, A, A, A, None, None, A,
                            ctypes.c_size_t(need.value), None) == 0
+
+
+def test_pack_validation(lib):
+    assert lib.moe_pack_rows(8, 64, A, B, None) == 2        # rows % 16
+    assert lib.moe_pack_rows(16, 96, A, B, None) == 2       # cols % 64
+    assert lib.moe_pack_rows(16, 64, None, B, None) == 1
+    assert lib.moe_pack_rows(16, 64, A, MIS, None) == 4
+    assert lib.moe_pack_rows(16, 64, A, A, None) == 6       # not in place
+    assert lib.moe_pack_rows(0, 64, A, B, None) == 0
 
 
 def test_quantize_validation(lib):

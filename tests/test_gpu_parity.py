@@ -9,13 +9,13 @@ import pytest
 import torch
 
 import workloads
-from int8_weight_moe_amd import (MoeError, moe_combine, moe_expert_ffn, moe_forward, moe_permute,
+from int8_weight_moe_amd import (MoeError, moe_combine, moe_expert_ffn, moe_forward, moe_pack_rows, moe_permute,
                                  moe_quantize_rows, moe_route)
 from int8_weight_moe_amd._lib import MOE_PATH_AUTO, MOE_PATH_STREAM, MOE_PATH_TILED
 from oracle import moe as omoe
 from oracle import quant as oquant
 from tests.helpers import (assert_close_to_oracle, check_routing, experts_to_device, np64,
-                           quantize_experts_oracle)
+                           quantize_experts_oracle, rowmajor_to_tiled, tiled_to_rowmajor)
 
 pytestmark = pytest.mark.gpu
 
@@ -48,6 +48,22 @@ def test_quantize_rows_bit_exact(src, scale):
     qr, sr = oquant.quantize_rows(np64(wt), scale)
     assert np.array_equal(q.cpu().numpy(), qr)
     assert np.array_equal(np64(s), sr)
+
+
+@pytest.mark.parametrize("rows,cols", [(16, 64), (48, 320), (3 * 512, 256), (16 * 64, 4096)])
+def test_pack_rows_is_the_documented_permutation(rows, cols):
+    rng = np.random.default_rng(rows + cols)
+    q = rng.integers(-127, 128, size=(rows, cols), dtype=np.int8)
+    p = moe_pack_rows(torch.from_numpy(q).cuda())
+    torch.cuda.synchronize()
+    got = p.cpu().numpy()
+    assert np.array_equal(got, rowmajor_to_tiled(q))
+    assert np.array_equal(tiled_to_rowmajor(got), q)
+    # spot-check the byte formula of the header directly
+    flat = got.reshape(-1)
+    for r, c in ((0, 0), (rows - 1, cols - 1), (17 % rows, 63), (5, 16 % cols)):
+        idx = ((r // 16) * (cols // 64) + c // 64) * 1024 + 256 * ((c % 64) // 16) + 16 * (r % 16) + c % 16
+        assert flat[idx] == q[r, c]
 
 
 # --------------------------------------------------------------------------- router

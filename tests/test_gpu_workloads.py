@@ -27,7 +27,7 @@ import workloads
 from int8_weight_moe_amd import MoeLayer, moe_combine, moe_expert_ffn, moe_permute, moe_route, quantize_experts
 from oracle import moe as omoe
 from oracle import quant as oquant
-from tests.helpers import assert_close_to_oracle, check_routing, np64
+from tests.helpers import assert_close_to_oracle, check_routing, np64, tiled_to_rowmajor
 
 pytestmark = pytest.mark.gpu
 
@@ -135,7 +135,7 @@ def test_sampled_outputs_against_oracle(run):
     for e in sample:
         for k in ("gate", "up", "down"):
             q, s = oquant.quantize_rows(np64(st["src"]["w_" + k][e]), w.scale)
-            qg = getattr(st["ex"], "q_" + k)[e].cpu().numpy()
+            qg = tiled_to_rowmajor(getattr(st["ex"], "q_" + k)[e].cpu().numpy())
             sg = np64(getattr(st["ex"], "s_" + k)[e])
             assert np.array_equal(qg, q), f"quantized codes differ (expert {e}, {k})"
             assert np.array_equal(sg, s), f"scales differ (expert {e}, {k})"
