@@ -75,9 +75,22 @@ __device__ __forceinline__ float load_scale(const void* s, long idx) {
   }
 }
 
-// SiLU in fp32: z / (1 + exp(-z)).
+// Four consecutive scales (idx % 4 == 0) as fp32, one vector load.
+template <bool kScaleBf16>
+__device__ __forceinline__ float4 load_scale4(const void* s, long idx) {
+  if constexpr (kScaleBf16) {
+    const uint2 b = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(s) + idx);
+    return make_float4(__uint_as_float(b.x << 16), __uint_as_float(b.x & 0xffff0000u), __uint_as_float(b.y << 16),
+                       __uint_as_float(b.y & 0xffff0000u));
+  } else {
+    return *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(s) + idx);
+  }
+}
+
+// SiLU in fp32: z / (1 + exp(-z)), with the hardware reciprocal (about 1 ulp);
+// the result is rounded to bf16 right after, so this costs no accuracy.
 __device__ __forceinline__ float silu(float z) {
-  return z / (1.0f + __expf(-z));
+  return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
 }
 
 // ---------------------------------------------------------------- activation loads

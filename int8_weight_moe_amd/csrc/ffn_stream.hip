@@ -97,15 +97,12 @@ __global__ __launch_bounds__(kStreamWaves * kWave) void ffn_stream_kernel(
     if constexpr (kGateUp) wp[ng][1] = W1 + off;
   }
   // per-lane scales of the 4 channels this lane holds in the result
-  float sc[NG][NMAT][4];
+  float4 sc[NG][NMAT];
 #pragma unroll
   for (int ng = 0; ng < NG; ++ng) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const long ch = (long)e * N + ch_base + ng * 16 + 4 * lg + r;
-      sc[ng][0][r] = load_scale<kScaleBf16>(S0, ch);
-      if constexpr (kGateUp) sc[ng][1][r] = load_scale<kScaleBf16>(S1, ch);
-    }
+    const long ch = (long)e * N + ch_base + ng * 16 + 4 * lg;
+    sc[ng][0] = load_scale4<kScaleBf16>(S0, ch);
+    if constexpr (kGateUp) sc[ng][1] = load_scale4<kScaleBf16>(S1, ch);
   }
 
   const int nsteps = Kd >> 6;
@@ -199,20 +196,15 @@ __global__ __launch_bounds__(kStreamWaves * kWave) void ffn_stream_kernel(
         for (int ng = 0; ng < NG; ++ng) {
           const int ch = ch_base + ng * 16 + 4 * lg;
           if constexpr (kGateUp) {
+            const float sgv[4] = {sc[ng][0].x, sc[ng][0].y, sc[ng][0].z, sc[ng][0].w};
+            const float suv[4] = {sc[ng][1].x, sc[ng][1].y, sc[ng][1].z, sc[ng][1].w};
             bf16x4 hv;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const float g = acc[rb][ng][0][q] * sc[ng][0][q];
-              const float u = acc[rb][ng][1][q] * sc[ng][1][q];
-              hv[q] = (__bf16)(silu(g) * u);
-            }
+            for (int q = 0; q < 4; ++q) hv[q] = (__bf16)(silu(acc[rb][ng][0][q] * sgv[q]) * (acc[rb][ng][1][q] * suv[q]));
             *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(out) + orow + ch) = hv;
           } else {
-            float4 yv;
-            yv.x = acc[rb][ng][0][0] * sc[ng][0][0];
-            yv.y = acc[rb][ng][0][1] * sc[ng][0][1];
-            yv.z = acc[rb][ng][0][2] * sc[ng][0][2];
-            yv.w = acc[rb][ng][0][3] * sc[ng][0][3];
+            const float4 yv = make_float4(acc[rb][ng][0][0] * sc[ng][0].x, acc[rb][ng][0][1] * sc[ng][0].y,
+                                          acc[rb][ng][0][2] * sc[ng][0].z, acc[rb][ng][0][3] * sc[ng][0].w);
             *reinterpret_cast<float4*>(static_cast<float*>(out) + orow + ch) = yv;
           }
         }

@@ -51,6 +51,10 @@ constexpr int kXcds = 8;
 #ifndef MOE_TILE_GM
 #define MOE_TILE_GM 4
 #endif
+// bf16 activations use the direct-to-LDS kernel below (1) or the register-staged one (0)
+#ifndef MOE_TILE_DMA
+#define MOE_TILE_DMA 1
+#endif
 
 __device__ __forceinline__ int swz(int row, int chunk) {
   return row * kBK + ((chunk ^ (row & 7)) << 3);
@@ -253,13 +257,12 @@ __global__ __launch_bounds__(WM * WN * kWave) void ffn_tiled_kernel(
       for (int j = 0; j < HALF; ++j) {
         const int ch = n0 + wn * (HALF * 16) + j * 16 + 4 * lg;
         if (ch >= N) continue;
+        const float4 sg = load_scale4<kScaleBf16>(S0, (long)e * N + ch);
+        const float4 su = load_scale4<kScaleBf16>(S1, (long)e * N + ch);
+        const float sgv[4] = {sg.x, sg.y, sg.z, sg.w}, suv[4] = {su.x, su.y, su.z, su.w};
         bf16x4 hv;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float g = acc[i][j][q] * load_scale<kScaleBf16>(S0, (long)e * N + ch + q);
-          const float u = acc[i][j + HALF][q] * load_scale<kScaleBf16>(S1, (long)e * N + ch + q);
-          hv[q] = (__bf16)(silu(g) * u);
-        }
+        for (int q = 0; q < 4; ++q) hv[q] = (__bf16)(silu(acc[i][j][q] * sgv[q]) * (acc[i][j + HALF][q] * suv[q]));
         *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(out) + orow + ch) = hv;
       }
     } else {
@@ -267,11 +270,292 @@ __global__ __launch_bounds__(WM * WN * kWave) void ffn_tiled_kernel(
       for (int j = 0; j < NB; ++j) {
         const int ch = n0 + wn * TN + j * 16 + 4 * lg;
         if (ch >= N) continue;
-        float4 yv;
-        yv.x = acc[i][j][0] * load_scale<kScaleBf16>(S0, (long)e * N + ch + 0);
-        yv.y = acc[i][j][1] * load_scale<kScaleBf16>(S0, (long)e * N + ch + 1);
-        yv.z = acc[i][j][2] * load_scale<kScaleBf16>(S0, (long)e * N + ch + 2);
-        yv.w = acc[i][j][3] * load_scale<kScaleBf16>(S0, (long)e * N + ch + 3);
+        const float4 sd = load_scale4<kScaleBf16>(S0, (long)e * N + ch);
+        const float4 yv = make_float4(acc[i][j][0] * sd.x, acc[i][j][1] * sd.y, acc[i][j][2] * sd.z, acc[i][j][3] * sd.w);
+        *reinterpret_cast<float4*>(static_cast<float*>(out) + orow + ch) = yv;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// bf16-activation kernel: operands reach LDS by direct global->LDS loads.
+//
+// Same tiles and tile order as above, but nothing is staged in registers: each
+// wave issues 16-byte global_load_lds instructions that write a contiguous
+// 1 KiB of LDS. A 3-stage LDS ring keeps the loads of the next two reduction
+// steps in flight while one is computed (per step: wait for this step's loads
+// with an explicit vmcnt, one barrier, issue the step two ahead, compute).
+//   activations: 256 rows x 128 bytes per step; instruction c of the tile
+//     covers rows 8c..8c+7, lane l writes row 8c + l/8, 16-byte chunk l%8,
+//     and fetches the logical chunk (l%8) ^ (row%8) -- so the tile lands in LDS
+//     already XOR-swizzled and the fragment reads stay conflict-free;
+//   weights: the tiled int8 layout is copied block for block (1 KiB per
+//     16-channel group and step) and stays int8 in LDS (half the bytes); a
+//     fragment is one 8-byte LDS read, converted to bf16 exactly in registers.
+// Rows past the expert's segment and channels past N load valid in-range
+// data whose results are never stored.
+// One 16-byte-per-lane global->LDS load: lane l reads base + voff (its own
+// 32-bit byte offset) and its 16 bytes land at LDS byte address lds + 16*l.
+// Written as inline asm with no output register and a memory clobber: the
+// compiler's own handling of these loads waits for all of them before every
+// LDS read, which would drain the ring; here the only waits are the explicit
+// vmcnt counts of the pipeline. m0 (the LDS base of the load) is set right
+// before each load; nothing else in these kernels uses m0. `base` and `lds`
+// are wave-uniform.
+__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff), "s"(base) : "memory");
+}
+
+// LDS byte address of a __shared__ object: the low 32 bits of its generic
+// address (the shared aperture base has zero low bits).
+template <typename T>
+__device__ __forceinline__ uint32_t lds_addr(const T* p) {
+  return (uint32_t)(uintptr_t)p;
+}
+
+// s_waitcnt immediate (gfx9 encoding): wait until at most `vm` vector-memory
+// operations are outstanding and all LDS operations have completed.
+constexpr int waitcnt_vm_lgkm0(int vm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4); }
+
+// Shape of the direct-to-LDS kernel: BM x BN tile, WM x WN waves, STAGES-deep ring.
+#ifndef MOE_DMA_BM
+#define MOE_DMA_BM 128
+#endif
+#ifndef MOE_DMA_BN
+#define MOE_DMA_BN 256
+#endif
+#ifndef MOE_DMA_WM
+#define MOE_DMA_WM 1
+#endif
+#ifndef MOE_DMA_WN
+#define MOE_DMA_WN 4
+#endif
+#ifndef MOE_DMA_STAGES
+#define MOE_DMA_STAGES 2
+#endif
+
+// Waves per SIMD the register allocation must leave room for: with 4-wave
+// workgroups two workgroups share a CU, so one can compute while the other
+// waits at its barrier.
+#ifndef MOE_DMA_WAVES_PER_EU
+#define MOE_DMA_WAVES_PER_EU 2
+#endif
+
+template <bool kGateUp, bool kScaleBf16, int GM, int BM, int BN, int WM, int WN, int STAGES>
+__global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(MOE_DMA_WAVES_PER_EU)))
+void ffn_tiled_dma_kernel(
+    const __bf16* __restrict__ X, const int32_t* __restrict__ sorted_slots, int topk,
+    const int8_t* __restrict__ W0, const int8_t* __restrict__ W1, const void* __restrict__ S0,
+    const void* __restrict__ S1, const int32_t* __restrict__ offsets, int E, int N, int Kd, int n_tiles_n,
+    int m_tiles, int total_blocks, void* __restrict__ out) {
+  constexpr int TM = BM / WM, TN = BN / WN, MB = TM / 16, NB = TN / 16;
+  static_assert(STAGES == 2 || STAGES == 3, "ring depth");
+  constexpr int A_STAGE = BM * 128;          // bytes per step (bf16, 64 wide)
+  constexpr int B_STAGE = BN * 64;           // bytes per step (int8, 64 wide)
+  constexpr int A_INSTR = A_STAGE / 1024 / (WM * WN);  // 1 KiB loads per wave per step
+  constexpr int B_INSTR = B_STAGE / 1024 / (WM * WN);
+  constexpr int CH_TILE = kGateUp ? BN / 2 : BN;
+  constexpr int VM_PER_STEP = A_INSTR + B_INSTR;
+  static_assert(A_INSTR * 1024 * WM * WN == A_STAGE && B_INSTR * 1024 * WM * WN == B_STAGE, "tile split");
+
+  __shared__ __attribute__((aligned(1024))) uint8_t As0[A_STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t As1[A_STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t As2[STAGES == 3 ? A_STAGE : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t Bs0[B_STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t Bs1[B_STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t Bs2[STAGES == 3 ? B_STAGE : 16];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: SGPR addressing
+  const int wm = wave / WN;
+  const int wn = wave % WN;
+  const int li = lane & 15;
+  const int lg = lane >> 4;
+
+  const int per_xcd = total_blocks / kXcds;
+  const int tile = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+  const int group_tiles = GM * n_tiles_n;
+  const int group = tile / group_tiles;
+  const int in_group = tile - group * group_tiles;
+  const int gm = min(GM, m_tiles - group * GM);
+  if (gm <= 0) return;
+  const int mt_global = group * GM + in_group % gm;
+  const int nt = in_group / gm;
+  if (nt >= n_tiles_n) return;
+  int e = -1, row0 = 0, nrows = 0;
+  {
+    int cum = 0;
+    for (int x = 0; x < E; ++x) {
+      const int o0 = offsets[x], o1 = offsets[x + 1];
+      const int mt_e = (o1 - o0 + BM - 1) / BM;
+      if (mt_global < cum + mt_e) {
+        e = x;
+        row0 = o0 + (mt_global - cum) * BM;
+        nrows = min(BM, o1 - row0);
+        break;
+      }
+      cum += mt_e;
+    }
+  }
+  if (e < 0) return;
+  const int n0 = nt * CH_TILE;
+
+  // activation sources: instruction j of this wave covers rows 8*(A_INSTR*wave + j) + lane/8;
+  // a_off = byte offset from X of this lane's 16 bytes at reduction step 0
+  uint32_t a_off[A_INSTR];
+#pragma unroll
+  for (int j = 0; j < A_INSTR; ++j) {
+    const int r = 8 * (A_INSTR * wave + j) + (lane >> 3);
+    const int rr = (r < nrows) ? r : 0;   // rows past the segment re-read row 0 (results unused)
+    uint32_t src_row;
+    if constexpr (kGateUp) {
+      src_row = (uint32_t)(sorted_slots[row0 + rr] / topk);
+    } else {
+      src_row = (uint32_t)(row0 + rr);
+    }
+    const int chunk = (lane & 7) ^ (r & 7);
+    a_off[j] = (src_row * (uint32_t)Kd + (uint32_t)(chunk * 8)) * 2u;
+  }
+  // weight sources: instruction j of this wave copies 16-channel block B_INSTR*wave + j of
+  // this expert's matrix (uniform base) at byte offset b_off (+1 KiB per step)
+  const int8_t* b_base[B_INSTR];
+  uint32_t b_off[B_INSTR];
+#pragma unroll
+  for (int j = 0; j < B_INSTR; ++j) {
+    const int blk = B_INSTR * wave + j;
+    const int8_t* base;
+    int chl;
+    if constexpr (kGateUp) {
+      base = (blk < BN / 32) ? W0 : W1;
+      chl = n0 + 16 * (blk % (BN / 32));
+    } else {
+      base = W0;
+      chl = n0 + 16 * blk;
+    }
+    if (chl >= N) chl = 0;                // past N: re-read channel group 0 (results unused)
+    b_base[j] = base + (long)e * N * Kd;
+    b_off[j] = (uint32_t)(chl >> 4) * (uint32_t)(Kd >> 6) * 1024u + 16u * lane;
+  }
+
+  // LDS buffers are always named directly (never through a pointer variable) so
+  // the compiler can tell the stages apart and does not drain the loads of the
+  // other stages before reading this one.
+#define MOE_DMA_ISSUE(KT, AS, BS)                                                                   \
+  {                                                                                                 \
+    _Pragma("unroll") for (int j = 0; j < A_INSTR; ++j)                                             \
+      dma16(X, a_off[j] + (uint32_t)(KT) * 128u, lds_addr(AS) + (A_INSTR * wave + j) * 1024);       \
+    _Pragma("unroll") for (int j = 0; j < B_INSTR; ++j)                                             \
+      dma16(b_base[j], b_off[j] + (uint32_t)(KT) * 1024u, lds_addr(BS) + (B_INSTR * wave + j) * 1024); \
+  }
+
+  // weight block of the wave's channel block j (LDS block index)
+  auto b_block = [&](int j) {
+    if constexpr (kGateUp) {
+      constexpr int HALF = NB / 2;
+      return (j < HALF) ? (wn * HALF + j) : (BN / 32 + wn * HALF + (j - HALF));
+    } else {
+      return wn * NB + j;
+    }
+  };
+
+  f32x4 acc[MB][NB];
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+// One 64-wide step: lane (li, lg) reads piece 16*lg + li of each weight block
+// (channel li, reduction bytes 16*lg .. +16; 16 lanes read 256 contiguous
+// bytes, free of bank conflicts) and uses its low half in sub-step 0 and its
+// high half in sub-step 1; the matching activation chunks are 2*lg + ks.
+#define MOE_DMA_COMPUTE(AS, BS)                                                                     \
+  {                                                                                                 \
+    uint4 wq[NB];                                                                                   \
+    _Pragma("unroll") for (int j = 0; j < NB; ++j)                                                  \
+      wq[j] = *reinterpret_cast<const uint4*>(&BS[b_block(j) * 1024 + 256 * lg + 16 * li]);        \
+    _Pragma("unroll") for (int ks = 0; ks < 2; ++ks) {                                              \
+      bf16x8 xf[MB];                                                                                \
+      bf16x8 wf[NB];                                                                                \
+      _Pragma("unroll") for (int i = 0; i < MB; ++i) {                                              \
+        const int row = wm * TM + i * 16 + li;                                                      \
+        const int chunk = (2 * lg + ks) ^ (row & 7);                                                \
+        xf[i] = *reinterpret_cast<const bf16x8*>(&AS[row * 128 + chunk * 16]);                      \
+      }                                                                                             \
+      _Pragma("unroll") for (int j = 0; j < NB; ++j)                                                \
+        wf[j] = ks == 0 ? i8x8_to_bf16(wq[j].x, wq[j].y) : i8x8_to_bf16(wq[j].z, wq[j].w);         \
+      _Pragma("unroll") for (int i = 0; i < MB; ++i)                                                \
+        _Pragma("unroll") for (int j = 0; j < NB; ++j) acc[i][j] = mfma_bf16(wf[j], xf[i], acc[i][j]); \
+    }                                                                                               \
+  }
+
+  const int nk = Kd >> 6;
+  // Every step issues the step STAGES-1 ahead, clamped to the last one: past the
+  // end this reloads the last step into a buffer that is no longer read, which
+  // keeps the loop free of branches around the loads and the vmcnt bookkeeping
+  // exact. Before computing step kt, its loads must be done while the loads of
+  // the STAGES-2 later steps may still be in flight.
+  constexpr int VM_IN_FLIGHT = (STAGES - 2) * VM_PER_STEP;
+#define MOE_DMA_STEP(KT, AC, BC, AN, BN_)                                                   \
+  {                                                                                         \
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(VM_IN_FLIGHT));                             \
+    __builtin_amdgcn_s_barrier();                                                           \
+    MOE_DMA_ISSUE(min((KT) + STAGES - 1, nk - 1), AN, BN_)                                  \
+    MOE_DMA_COMPUTE(AC, BC)                                                                 \
+  }
+  int k0 = 0;
+  if constexpr (STAGES == 3) {
+    MOE_DMA_ISSUE(0, As0, Bs0)
+    MOE_DMA_ISSUE(min(1, nk - 1), As1, Bs1)
+    for (; k0 + 3 <= nk; k0 += 3) {
+      MOE_DMA_STEP(k0 + 0, As0, Bs0, As2, Bs2)
+      MOE_DMA_STEP(k0 + 1, As1, Bs1, As0, Bs0)
+      MOE_DMA_STEP(k0 + 2, As2, Bs2, As1, Bs1)
+    }
+    if (k0 < nk) MOE_DMA_STEP(k0, As0, Bs0, As2, Bs2)
+    if (k0 + 1 < nk) MOE_DMA_STEP(k0 + 1, As1, Bs1, As0, Bs0)
+  } else {
+    MOE_DMA_ISSUE(0, As0, Bs0)
+    for (; k0 + 2 <= nk; k0 += 2) {
+      MOE_DMA_STEP(k0 + 0, As0, Bs0, As1, Bs1)
+      MOE_DMA_STEP(k0 + 1, As1, Bs1, As0, Bs0)
+    }
+    if (k0 < nk) MOE_DMA_STEP(k0, As0, Bs0, As1, Bs1)
+  }
+#undef MOE_DMA_STEP
+  // no load may still be writing this workgroup's LDS when the waves exit
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+#undef MOE_DMA_ISSUE
+#undef MOE_DMA_COMPUTE
+
+  // ---- epilogue (as in the register-staged kernel)
+#pragma unroll
+  for (int i = 0; i < MB; ++i) {
+    const int r = wm * TM + i * 16 + li;
+    if (r >= nrows) continue;
+    const long orow = (long)(row0 + r) * N;
+    if constexpr (kGateUp) {
+      constexpr int HALF = NB / 2;
+#pragma unroll
+      for (int j = 0; j < HALF; ++j) {
+        const int ch = n0 + wn * (HALF * 16) + j * 16 + 4 * lg;
+        if (ch >= N) continue;
+        const float4 sg = load_scale4<kScaleBf16>(S0, (long)e * N + ch);
+        const float4 su = load_scale4<kScaleBf16>(S1, (long)e * N + ch);
+        const float sgv[4] = {sg.x, sg.y, sg.z, sg.w}, suv[4] = {su.x, su.y, su.z, su.w};
+        bf16x4 hv;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) hv[q] = (__bf16)(silu(acc[i][j][q] * sgv[q]) * (acc[i][j + HALF][q] * suv[q]));
+        *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(out) + orow + ch) = hv;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        const int ch = n0 + wn * TN + j * 16 + 4 * lg;
+        if (ch >= N) continue;
+        const float4 sd = load_scale4<kScaleBf16>(S0, (long)e * N + ch);
+        const float4 yv = make_float4(acc[i][j][0] * sd.x, acc[i][j][1] * sd.y, acc[i][j][2] * sd.z, acc[i][j][3] * sd.w);
         *reinterpret_cast<float4*>(static_cast<float*>(out) + orow + ch) = yv;
       }
     }
@@ -291,6 +575,30 @@ hipError_t launch_tiled_pass(const FfnArgs& a, hipStream_t stream) {
   blocks = (blocks + kXcds - 1) / kXcds * kXcds;
   const dim3 grid((unsigned)blocks);
   const dim3 block(WM * WN * kWave);
+  // the direct-to-LDS kernel addresses with 32-bit byte offsets from the
+  // activation tensor and from one expert's weight matrix
+  const uint64_t act_bytes = kGateUp ? (uint64_t)a.T * a.d * 2 : (uint64_t)a.S * a.f * 2;
+  const bool offsets_fit = act_bytes < (1ull << 32) && (uint64_t)N * Kd < (1ull << 32);
+  if (sizeof(Act) == 2 && MOE_TILE_DMA && offsets_fit) {
+    constexpr int DBM = MOE_DMA_BM, DBN = MOE_DMA_BN, DWM = MOE_DMA_WM, DWN = MOE_DMA_WN, DST = MOE_DMA_STAGES;
+    constexpr int DCH = kGateUp ? DBN / 2 : DBN;
+    const int dn_tiles = (N + DCH - 1) / DCH;
+    const long dm_tiles = (long)(a.S + DBM - 1) / DBM + a.E;
+    long dblocks = (dm_tiles * dn_tiles + kXcds - 1) / kXcds * kXcds;
+    const dim3 dblock(DWM * DWN * kWave);
+    if constexpr (kGateUp) {
+      hipLaunchKernelGGL((ffn_tiled_dma_kernel<true, kScaleBf16, GM, DBM, DBN, DWM, DWN, DST>), dim3((unsigned)dblocks),
+                         dblock, 0, stream, static_cast<const __bf16*>(a.x), a.sorted_slots, a.K, a.w_gate, a.w_up,
+                         a.s_gate, a.s_up, a.offsets, a.E, N, Kd, dn_tiles, (int)dm_tiles, (int)dblocks,
+                         static_cast<void*>(a.h));
+    } else {
+      hipLaunchKernelGGL((ffn_tiled_dma_kernel<false, kScaleBf16, GM, DBM, DBN, DWM, DWN, DST>), dim3((unsigned)dblocks),
+                         dblock, 0, stream, static_cast<const __bf16*>(a.h), a.sorted_slots, a.K, a.w_down, nullptr,
+                         a.s_down, nullptr, a.offsets, a.E, N, Kd, dn_tiles, (int)dm_tiles, (int)dblocks,
+                         static_cast<void*>(a.y_rows));
+    }
+    return hipGetLastError();
+  }
   if constexpr (kGateUp) {
     hipLaunchKernelGGL((ffn_tiled_kernel<true, Act, kScaleBf16, BM, BN, WM, WN, GM>), grid, block, 0, stream,
                        static_cast<const Act*>(a.x), a.sorted_slots, a.K, a.w_gate, a.w_up, a.s_gate, a.s_up,
