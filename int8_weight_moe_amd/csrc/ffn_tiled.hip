@@ -470,7 +470,7 @@ void ffn_tiled_dma_kernel(
 // (channel li, reduction bytes 16*lg .. +16; 16 lanes read 256 contiguous
 // bytes, free of bank conflicts) and uses its low half in sub-step 0 and its
 // high half in sub-step 1; the matching activation chunks are 2*lg + ks.
-#define MOE_DMA_COMPUTE(AS, BS)                                                                     \
+#define MOE_DMA_COMPUTE(AS, BS, MBV)                                                                \
   {                                                                                                 \
     uint4 wq[NB];                                                                                   \
     _Pragma("unroll") for (int j = 0; j < NB; ++j)                                                  \
@@ -479,16 +479,41 @@ void ffn_tiled_dma_kernel(
       bf16x8 xf[MB];                                                                                \
       bf16x8 wf[NB];                                                                                \
       _Pragma("unroll") for (int i = 0; i < MB; ++i) {                                              \
-        const int row = wm * TM + i * 16 + li;                                                      \
-        const int chunk = (2 * lg + ks) ^ (row & 7);                                                \
-        xf[i] = *reinterpret_cast<const bf16x8*>(&AS[row * 128 + chunk * 16]);                      \
+        if (i < (MBV)) {                                                                            \
+          const int row = wm * TM + i * 16 + li;                                                    \
+          const int chunk = (2 * lg + ks) ^ (row & 7);                                              \
+          xf[i] = *reinterpret_cast<const bf16x8*>(&AS[row * 128 + chunk * 16]);                    \
+        }                                                                                           \
       }                                                                                             \
-      _Pragma("unroll") for (int j = 0; j < NB; ++j)                                                \
-        wf[j] = ks == 0 ? i8x8_to_bf16(wq[j].x, wq[j].y) : i8x8_to_bf16(wq[j].z, wq[j].w);         \
-      _Pragma("unroll") for (int i = 0; i < MB; ++i)                                                \
-        _Pragma("unroll") for (int j = 0; j < NB; ++j) acc[i][j] = mfma_bf16(wf[j], xf[i], acc[i][j]); \
+      MOE_DMA_MMA(MBV)                                                                              \
     }                                                                                               \
   }
+
+// The MFMAs of one sub-step. Variant 0: all weight fragments converted, then
+// the i-j MFMA nest. Variant 1: fragment j converted right before its MFMAs
+// (j outer). Variant 2: as 1, with scheduling groups pinning the interleave.
+#ifndef MOE_DMA_SCHED
+#define MOE_DMA_SCHED 0
+#endif
+#if MOE_DMA_SCHED == 0
+#define MOE_DMA_MMA(MBV)                                                                            \
+  _Pragma("unroll") for (int j = 0; j < NB; ++j)                                                    \
+    wf[j] = ks == 0 ? i8x8_to_bf16(wq[j].x, wq[j].y) : i8x8_to_bf16(wq[j].z, wq[j].w);             \
+  _Pragma("unroll") for (int i = 0; i < MB; ++i)                                                    \
+    if (i < (MBV))                                                                                  \
+      _Pragma("unroll") for (int j = 0; j < NB; ++j) acc[i][j] = mfma_bf16(wf[j], xf[i], acc[i][j]);
+#else
+#define MOE_DMA_MMA(MBV)                                                                            \
+  _Pragma("unroll") for (int j = 0; j < NB; ++j) {                                                  \
+    wf[j] = ks == 0 ? i8x8_to_bf16(wq[j].x, wq[j].y) : i8x8_to_bf16(wq[j].z, wq[j].w);             \
+    _Pragma("unroll") for (int i = 0; i < MB; ++i)                                                  \
+      if (i < (MBV)) acc[i][j] = mfma_bf16(wf[j], xf[i], acc[i][j]);                                \
+    if (MOE_DMA_SCHED == 2) {                                                                       \
+      __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);                                           \
+      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);                                            \
+    }                                                                                               \
+  }
+#endif
 
   const int nk = Kd >> 6;
   // Every step issues the step STAGES-1 ahead, clamped to the last one: past the
@@ -497,32 +522,44 @@ void ffn_tiled_dma_kernel(
   // exact. Before computing step kt, its loads must be done while the loads of
   // the STAGES-2 later steps may still be in flight.
   constexpr int VM_IN_FLIGHT = (STAGES - 2) * VM_PER_STEP;
-#define MOE_DMA_STEP(KT, AC, BC, AN, BN_)                                                   \
+#define MOE_DMA_STEP(KT, AC, BC, AN, BN_, MBV)                                              \
   {                                                                                         \
     __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(VM_IN_FLIGHT));                             \
     __builtin_amdgcn_s_barrier();                                                           \
     MOE_DMA_ISSUE(min((KT) + STAGES - 1, nk - 1), AN, BN_)                                  \
-    MOE_DMA_COMPUTE(AC, BC)                                                                 \
+    MOE_DMA_COMPUTE(AC, BC, MBV)                                                            \
   }
-  int k0 = 0;
-  if constexpr (STAGES == 3) {
-    MOE_DMA_ISSUE(0, As0, Bs0)
-    MOE_DMA_ISSUE(min(1, nk - 1), As1, Bs1)
-    for (; k0 + 3 <= nk; k0 += 3) {
-      MOE_DMA_STEP(k0 + 0, As0, Bs0, As2, Bs2)
-      MOE_DMA_STEP(k0 + 1, As1, Bs1, As0, Bs0)
-      MOE_DMA_STEP(k0 + 2, As2, Bs2, As1, Bs1)
-    }
-    if (k0 < nk) MOE_DMA_STEP(k0, As0, Bs0, As2, Bs2)
-    if (k0 + 1 < nk) MOE_DMA_STEP(k0 + 1, As1, Bs1, As0, Bs0)
+  // A partial row tile (the last one of an expert) skips the MFMAs and the
+  // fragment reads of the 16-row blocks it does not have, in this wave's rows.
+  const int mb_valid = min(MB, max(0, (nrows - wm * TM + 15) / 16));
+#define MOE_DMA_MAIN_LOOP(MBV)                                                              \
+  {                                                                                         \
+    int k0 = 0;                                                                             \
+    if constexpr (STAGES == 3) {                                                            \
+      MOE_DMA_ISSUE(0, As0, Bs0)                                                            \
+      MOE_DMA_ISSUE(min(1, nk - 1), As1, Bs1)                                               \
+      for (; k0 + 3 <= nk; k0 += 3) {                                                       \
+        MOE_DMA_STEP(k0 + 0, As0, Bs0, As2, Bs2, MBV)                                       \
+        MOE_DMA_STEP(k0 + 1, As1, Bs1, As0, Bs0, MBV)                                       \
+        MOE_DMA_STEP(k0 + 2, As2, Bs2, As1, Bs1, MBV)                                       \
+      }                                                                                     \
+      if (k0 < nk) MOE_DMA_STEP(k0, As0, Bs0, As2, Bs2, MBV)                                \
+      if (k0 + 1 < nk) MOE_DMA_STEP(k0 + 1, As1, Bs1, As0, Bs0, MBV)                        \
+    } else {                                                                                \
+      MOE_DMA_ISSUE(0, As0, Bs0)                                                            \
+      for (; k0 + 2 <= nk; k0 += 2) {                                                       \
+        MOE_DMA_STEP(k0 + 0, As0, Bs0, As1, Bs1, MBV)                                       \
+        MOE_DMA_STEP(k0 + 1, As1, Bs1, As0, Bs0, MBV)                                       \
+      }                                                                                     \
+      if (k0 < nk) MOE_DMA_STEP(k0, As0, Bs0, As1, Bs1, MBV)                                \
+    }                                                                                       \
+  }
+  if (mb_valid == MB) {
+    MOE_DMA_MAIN_LOOP(MB)
   } else {
-    MOE_DMA_ISSUE(0, As0, Bs0)
-    for (; k0 + 2 <= nk; k0 += 2) {
-      MOE_DMA_STEP(k0 + 0, As0, Bs0, As1, Bs1)
-      MOE_DMA_STEP(k0 + 1, As1, Bs1, As0, Bs0)
-    }
-    if (k0 < nk) MOE_DMA_STEP(k0, As0, Bs0, As1, Bs1)
+    MOE_DMA_MAIN_LOOP(mb_valid)
   }
+#undef MOE_DMA_MAIN_LOOP
 #undef MOE_DMA_STEP
   // no load may still be writing this workgroup's LDS when the waves exit
   __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
