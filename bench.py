@@ -34,7 +34,8 @@ HBM_PEAK_GBPS = 8000.0       # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 
 # decode workload -> the prefill workload with the same weights
-SIBLING = {"mini-decode": "mini-prefill", "large-decode": "large-prefill-skewed"}
+SIBLING = {"mini-decode": "mini-prefill", "large-decode": "large-prefill-skewed",
+           "large-mlp-decode": "large-mlp-prefill"}
 
 
 def parse():
@@ -102,59 +103,83 @@ def algorithmic(w, counts):
 
 
 def ffn_path_used(w, path):
-    """Schedule the library runs: it streams weights when T*K <= 48*E rows (decode-sized)."""
+    """Schedule the library runs: it streams weights when T*K <= 64*E rows (decode-sized)."""
     from int8_weight_moe_amd._lib import MOE_PATH_AUTO, MOE_PATH_STREAM
-    if path == MOE_PATH_STREAM or (path == MOE_PATH_AUTO and w.T * w.K <= 48 * w.E):
+    if path == MOE_PATH_STREAM or (path == MOE_PATH_AUTO and w.T * w.K <= 64 * w.E):
         return "stream"
     return "tiled"
 
 
 # ----------------------------------------------------------------------------- timing
-def time_forward(layer, x, path, steps, warmup):
+def time_forward(layer, x, path, steps, warmup, dense=False):
+    """Average step time of the fused call: moe_forward, or moe_mlp_forward for a dense MLP layer."""
     import torch
+    from int8_weight_moe_amd import moe_mlp_forward
     y = torch.empty_like(x)
     ids = torch.empty((x.shape[0], layer.K), dtype=torch.int32, device=x.device)
     gw = torch.empty((x.shape[0], layer.K), dtype=torch.float32, device=x.device)
+    ws = layer.workspace(layer.shape(x, path))
+
+    def step():
+        if dense:
+            moe_mlp_forward(x, layer.experts, path=path, y=y, workspace=ws)
+        else:
+            layer.forward(x, path=path, y=y, ids=ids, w=gw)
+
     for _ in range(warmup):
-        layer.forward(x, path=path, y=y, ids=ids, w=gw)
+        step()
     torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     start.record()
     for _ in range(steps):
-        layer.forward(x, path=path, y=y, ids=ids, w=gw)
+        step()
     end.record()
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) * 1e3 / steps
     return start.elapsed_time(end) / steps, wall
 
 
-def time_stages(layer, x, path, steps, warmup):
-    """Average duration (us) of each kernel of the step, HIP events on the launch stream."""
+def time_stages(layer, x, path, steps, warmup, dense=False):
+    """Average duration (us) of each kernel of the step, HIP events on the launch stream.
+
+    A dense MLP layer has no routing: its row layout (every token once, weight
+    1) is set up once, outside the timed stages, and only the FFN passes and
+    the combine are timed."""
     import torch
     from int8_weight_moe_amd import moe_combine, moe_expert_down, moe_expert_gate_up, moe_permute, moe_route
     ex, K = layer.experts, layer.K
     T = x.shape[0]
-    names = ["route", "permute", "gate_up", "down", "combine"]
+    names = ["gate_up", "down", "combine"] if dense else ["route", "permute", "gate_up", "down", "combine"]
     h = torch.empty((T * K, ex.f), dtype=torch.bfloat16, device=x.device)
     rows = torch.empty((T * K, ex.d), dtype=torch.float32, device=x.device)
+    if dense:
+        ids0, gw0 = moe_route(x, layer.router_w, layer.bias, K)
+        layout = (gw0,) + tuple(moe_permute(ids0, ex.E))
 
     def step(ev):
-        ev[0].record()
-        ids, gw = moe_route(x, layer.router_w, layer.bias, K)
-        ev[1].record()
-        off, ss, s2r = moe_permute(ids, ex.E)
-        ev[2].record()
+        i = 0
+        ev[i].record()
+        if dense:
+            gw, off, ss, s2r = layout
+        else:
+            ids, gw = moe_route(x, layer.router_w, layer.bias, K)
+            i += 1
+            ev[i].record()
+            off, ss, s2r = moe_permute(ids, ex.E)
+            i += 1
+            ev[i].record()
         moe_expert_gate_up(x, off, ss, ex, K, path=path, h=h)
-        ev[3].record()
+        ev[i + 1].record()
         moe_expert_down(h, off, ex, T, K, act=x.dtype, path=path, y_rows=rows)
-        ev[4].record()
+        ev[i + 2].record()
         moe_combine(rows, s2r, gw, x.dtype)
-        ev[5].record()
+        ev[i + 3].record()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
+    n_ev = len(names) + 1
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(steps)]
     for _ in range(warmup):
-        step([torch.cuda.Event(enable_timing=True) for _ in range(6)])
+        step([torch.cuda.Event(enable_timing=True) for _ in range(n_ev)])
     torch.cuda.synchronize()
     for i in range(steps):
         step(evs[i])
@@ -270,7 +295,8 @@ def main():
     from int8_weight_moe_amd._lib import MOE_PATH_AUTO, MOE_PATH_STREAM, MOE_PATH_TILED
 
     path = {"auto": MOE_PATH_AUTO, "stream": MOE_PATH_STREAM, "tiled": MOE_PATH_TILED}[args.path]
-    w = workloads.WORKLOADS[args.workload]
+    w = workloads.ALL_WORKLOADS[args.workload]
+    dense = args.workload in workloads.DENSE_WORKLOADS
     dev = torch.device("cuda:0")
     log(f"workload {w.name}: T={w.T} d={w.d} f={w.f} E={w.E} K={w.K}")
     layer, src, qms = build_layer(w, dev)
@@ -280,16 +306,16 @@ def main():
     counts = touched_rows(layer, x, path)
     alg = algorithmic(w, counts)
 
-    ms, wall_ms = time_forward(layer, x, path, args.steps, args.warmup)
+    ms, wall_ms = time_forward(layer, x, path, args.steps, args.warmup, dense)
     log(f"forward: {ms * 1e3:.1f} us/step (wall {wall_ms * 1e3:.1f} us)")
-    stages = time_stages(layer, x, path, args.steps, args.warmup)
+    stages = time_stages(layer, x, path, args.steps, args.warmup, dense)
     log("stages (us): " + ", ".join(f"{k}={v:.1f}" for k, v in stages.items()))
     dominant = max(("gate_up", "down"), key=lambda k: stages[k])
     used_path = ffn_path_used(w, path)
 
     layer_s = ms * 1e-3
     result = {
-        "metric": "MoE-layer tokens/s",
+        "metric": "MLP-layer tokens/s" if dense else "MoE-layer tokens/s",
         "value": round(w.T / layer_s, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -316,7 +342,7 @@ def main():
 
     sib = SIBLING.get(w.name)
     if sib and not args.no_prefill:
-        wp = workloads.WORKLOADS[sib]
+        wp = workloads.ALL_WORKLOADS[sib]
         if (wp.d, wp.f, wp.E) == (w.d, w.f, w.E):
             orig_bias = layer.bias
             if wp.has_bias:
@@ -324,8 +350,8 @@ def main():
             xp = workloads.draw_activations(wp).to(dev)
             cp = touched_rows(layer, xp, MOE_PATH_AUTO)
             ap_ = algorithmic(wp, cp)
-            pms, _ = time_forward(layer, xp, MOE_PATH_AUTO, args.prefill_steps, 2)
-            pst = time_stages(layer, xp, MOE_PATH_AUTO, max(3, args.prefill_steps // 2), 1)
+            pms, _ = time_forward(layer, xp, MOE_PATH_AUTO, args.prefill_steps, 2, dense)
+            pst = time_stages(layer, xp, MOE_PATH_AUTO, max(3, args.prefill_steps // 2), 1, dense)
             pdom = max(("gate_up", "down"), key=lambda k: pst[k])
             log(f"prefill {wp.name}: {pms:.3f} ms/step; stages (us): "
                 + ", ".join(f"{k}={v:.1f}" for k, v in pst.items()))

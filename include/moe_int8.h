@@ -67,9 +67,10 @@ enum {
 /* dtype codes */
 enum { MOE_F32 = 0, MOE_BF16 = 1 };
 
-/* expert-FFN schedule: AUTO picks STREAM when few rows fall on each expert
- * (decode) and TILED otherwise (prefill). Both give results within the same
- * tolerance of the exact layer; they are not bit-identical to each other. */
+/* expert-FFN schedule: AUTO picks STREAM when at most 64 rows fall on each
+ * expert on average (T*K <= 64*E: decode) and TILED otherwise (prefill).
+ * Both give results within the same tolerance of the exact layer; they are
+ * not bit-identical to each other. Each is deterministic. */
 enum { MOE_PATH_AUTO = 0, MOE_PATH_STREAM = 1, MOE_PATH_TILED = 2 };
 
 typedef struct moe_shape {
@@ -164,6 +165,19 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const void* router
                        const void* s_gate, const void* s_up, const void* s_down,
                        void* y, int32_t* topk_ids_out, float* topk_w_out,
                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Dense int8-weight MLP (Jamba-1.5 paper, "Serving Considerations and
+ * Improvements": ExpertsInt8 quantizes the MoE *and* the MLP weights). An MLP
+ * layer is the MoE layer with one expert used by every token with weight 1:
+ *   y = s_d * (q_d . h),  h = silu(s_g * (q_g . x)) * (s_u * (q_u . x)).
+ * shape->E and shape->K must be 1; no router. Same kernels and layouts as the
+ * MoE calls (weights in the tiled int8 layout), same tolerance.
+ *   y [T, d] act_dtype out; workspace >= moe_mlp_workspace_size bytes. */
+moe_status moe_mlp_workspace_size(const moe_shape* shape, size_t* bytes);
+moe_status moe_mlp_forward(const moe_shape* shape, const void* x,
+                           const int8_t* w_gate, const int8_t* w_up, const int8_t* w_down,
+                           const void* s_gate, const void* s_up, const void* s_down, void* y,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ExpertsInt8 quantizer (paper: "Serving Considerations and Improvements":
  * quantized at load time in seconds, no calibration). Row-wise symmetric int8:

@@ -8,8 +8,8 @@ takes torch tensors for device memory and streams.
 """
 from ._lib import LIB_PATH, MoeError, load  # noqa: F401
 from .ops import (Int8Experts, MoeLayer, moe_combine, moe_expert_down, moe_expert_ffn, moe_expert_gate_up,  # noqa: F401
-                  moe_forward, moe_pack_rows, moe_permute, moe_quantize_rows, moe_route, pack_experts,
+                  moe_forward, moe_mlp_forward, moe_pack_rows, moe_permute, moe_quantize_rows, moe_route, pack_experts,
                   quantize_experts)
 
-__all__ = ["Int8Experts", "MoeLayer", "moe_route", "moe_permute", "moe_expert_ffn", "moe_expert_gate_up", "moe_expert_down", "moe_combine", "moe_forward",
+__all__ = ["Int8Experts", "MoeLayer", "moe_route", "moe_permute", "moe_expert_ffn", "moe_expert_gate_up", "moe_expert_down", "moe_combine", "moe_forward", "moe_mlp_forward",
            "moe_quantize_rows", "moe_pack_rows", "pack_experts", "quantize_experts", "MoeError", "load", "LIB_PATH"]

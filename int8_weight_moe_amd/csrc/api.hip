@@ -32,7 +32,7 @@ constexpr size_t kAlign = 256;
 size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 // Rows at or below this many per expert (on average) go to the weight-streaming schedule.
-constexpr long kStreamRowsPerExpert = 48;
+constexpr long kStreamRowsPerExpert = 64;
 
 moe_status check_shape(const moe_shape* s) {
   if (!s) return fail(MOE_ERR_NULL, "shape is NULL");
@@ -309,6 +309,53 @@ moe_status moe_forward(const moe_shape* s, const void* x, const void* router_w, 
   st = run_down(s, a, stream);
   if (st != MOE_OK) return st;
   e = moe::launch_combine(y_rows, s2r, wts, s->T, s->d, s->K, s->act_dtype == MOE_BF16, y, stream);
+  if (e != hipSuccess) return hip_fail(e, "combine launch");
+  return MOE_OK;
+}
+
+moe_status moe_mlp_workspace_size(const moe_shape* shape, size_t* bytes) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (!bytes) return fail(MOE_ERR_NULL, "bytes is NULL");
+  if (shape->E != 1 || shape->K != 1) return fail(MOE_ERR_SHAPE, "the dense MLP needs E = K = 1");
+  *bytes = forward_layout(shape).total;
+  return MOE_OK;
+}
+
+moe_status moe_mlp_forward(const moe_shape* s, const void* x, const int8_t* w_gate, const int8_t* w_up,
+                           const int8_t* w_down, const void* s_gate, const void* s_up, const void* s_down, void* y,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (s->E != 1 || s->K != 1) return fail(MOE_ERR_SHAPE, "the dense MLP needs E = K = 1 (E=%d, K=%d)", s->E, s->K);
+  REQUIRE_PTR(x);
+  REQUIRE_PTR(w_gate);
+  REQUIRE_PTR(w_up);
+  REQUIRE_PTR(w_down);
+  REQUIRE_PTR(s_gate);
+  REQUIRE_PTR(s_up);
+  REQUIRE_PTR(s_down);
+  REQUIRE_PTR(y);
+  REQUIRE_PTR(workspace);
+  const WsLayout L = forward_layout(s);
+  if (workspace_bytes < L.total)
+    return fail(MOE_ERR_WORKSPACE, "workspace_bytes=%zu < required %zu", workspace_bytes, L.total);
+  if (s->T == 0) return MOE_OK;
+  char* ws = static_cast<char*>(workspace);
+  float* wts = reinterpret_cast<float*>(ws + L.w);
+  int32_t* offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
+  int32_t* sorted = reinterpret_cast<int32_t*>(ws + L.sorted);
+  int32_t* s2r = reinterpret_cast<int32_t*>(ws + L.s2r);
+  __bf16* h = reinterpret_cast<__bf16*>(ws + L.h);
+  float* y_rows = reinterpret_cast<float*>(ws + L.y_rows);
+  hipError_t e = moe::launch_dense_init(s->T, offsets, sorted, s2r, wts, stream);
+  if (e != hipSuccess) return hip_fail(e, "dense init launch");
+  const moe::FfnArgs a = ffn_args(s, x, offsets, sorted, w_gate, w_up, w_down, s_gate, s_up, s_down, y_rows, h);
+  st = run_gate_up(s, a, stream);
+  if (st != MOE_OK) return st;
+  st = run_down(s, a, stream);
+  if (st != MOE_OK) return st;
+  e = moe::launch_combine(y_rows, s2r, wts, s->T, s->d, 1, s->act_dtype == MOE_BF16, y, stream);
   if (e != hipSuccess) return hip_fail(e, "combine launch");
   return MOE_OK;
 }

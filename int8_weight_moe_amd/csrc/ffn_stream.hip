@@ -16,6 +16,11 @@
 //     activation elements 0-7 of the same lane group, bytes 8-15 with 8-15.
 // Items are numbered over the experts that received rows only, so the grid
 // has no idle waves for untouched experts.
+// With few experts (a dense MLP layer: one) there are too few items to keep
+// enough loads in flight, so the reduction axis of each item is cut into KS
+// slices streamed by the KS waves of one workgroup; the slices' fp32 partial
+// sums are added through LDS in ascending slice order before the epilogue, so
+// the result does not depend on scheduling and costs no extra HBM traffic.
 // Gate/up pass: g and u accumulate side by side; the epilogue applies the
 // per-channel scales and SwiGLU and stores h (bf16). Down pass: the epilogue
 // applies the down scale and stores y_rows (fp32).
@@ -40,6 +45,11 @@ namespace {
 #ifndef MOE_STREAM_NG_DN
 #define MOE_STREAM_NG_DN 4
 #endif
+// down-pass groups per wave of the 64-row variant (its accumulators and
+// activation ring are four times larger)
+#ifndef MOE_STREAM_NG_DN_WIDE
+#define MOE_STREAM_NG_DN_WIDE 2
+#endif
 #ifndef MOE_STREAM_P_DN
 #define MOE_STREAM_P_DN 4
 #endif
@@ -49,15 +59,49 @@ namespace {
 #ifndef MOE_STREAM_WAVES
 #define MOE_STREAM_WAVES 4
 #endif
+// Waves a pass wants in flight: the 32-row variant MIN_WAVES, the 64-row
+// variant MIN_WAVES_WIDE (four times the MFMA and activation work per weight
+// byte, so more waves are needed to keep HBM busy).
+#ifndef MOE_STREAM_MIN_WAVES
+#define MOE_STREAM_MIN_WAVES 1024
+#endif
+#ifndef MOE_STREAM_MIN_WAVES_WIDE
+#define MOE_STREAM_MIN_WAVES_WIDE 4096
+#endif
+// activation prefetch ring of the 64-row variant (see the main loop)
+#ifndef MOE_STREAM_PA_WIDE
+#define MOE_STREAM_PA_WIDE 2
+#endif
 constexpr int kStreamWaves = MOE_STREAM_WAVES;
 
-template <bool kGateUp, typename Act, bool kScaleBf16, int NG, int RB, int P>
-__global__ __launch_bounds__(kStreamWaves * kWave) void ffn_stream_kernel(
+constexpr int ring_gcd(int a, int b) { return b == 0 ? a : ring_gcd(b, a % b); }
+constexpr int ring_unroll(int a, int b) { return a / ring_gcd(a, b) * b; }
+
+// Reduction split (1, 2, 4 or 8) of a pass with `items` (expert, channel
+// group) items.
+int choose_split(long items, int RB) {
+  const long want = RB >= 4 ? MOE_STREAM_MIN_WAVES_WIDE : MOE_STREAM_MIN_WAVES;
+  int ks = 1;
+  while (ks < 8 && items * ks < want) ks *= 2;
+  return ks;
+}
+
+// Waves of a workgroup: kStreamWaves items of one wave each (KS = 1), or the
+// KS slices of one item (KS > 1).
+constexpr int stream_block_waves(int KS) { return KS > 1 ? KS : kStreamWaves; }
+
+// A workgroup holds stream_block_waves(KS)/KS items; wave w works on item
+// w/KS and streams the (w%KS)-th slice of its reduction axis.
+template <bool kGateUp, typename Act, bool kScaleBf16, int NG, int RB, int P, int KS>
+__global__ __launch_bounds__(stream_block_waves(KS) * kWave) void ffn_stream_kernel(
     const Act* __restrict__ X, const int32_t* __restrict__ sorted_slots, int topk,
     const int8_t* __restrict__ W0, const int8_t* __restrict__ W1, const void* __restrict__ S0,
     const void* __restrict__ S1, const int32_t* __restrict__ offsets, int E, int N, int Kd,
     void* __restrict__ out) {
   constexpr int NMAT = kGateUp ? 2 : 1;
+  constexpr int IPW = stream_block_waves(KS) / KS;  // items per workgroup
+  // partial sums of slices 1..KS-1 for one 16-row block (KS > 1: one item)
+  __shared__ f32x4 red[KS > 1 ? KS - 1 : 1][NG][NMAT][kWave];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int li = lane & 15;
@@ -65,7 +109,9 @@ __global__ __launch_bounds__(kStreamWaves * kWave) void ffn_stream_kernel(
 
   // ---- item -> (expert among the touched ones, channel group)
   const int gpe = N / (16 * NG);
-  const int item = blockIdx.x * kStreamWaves + wave;
+  const int witem = wave / KS;  // item within the workgroup
+  const int item = blockIdx.x * IPW + witem;
+  const int kslice = wave % KS;
   const int te = item / gpe;
   const int grp = item - te * gpe;
   int e = -1, row0 = 0, nrows = 0;
@@ -84,6 +130,8 @@ __global__ __launch_bounds__(kStreamWaves * kWave) void ffn_stream_kernel(
       }
     }
   }
+  // With KS > 1 the workgroup is one item: every wave takes this return, the
+  // row loop and the barriers below together.
   if (e < 0) return;
 
   const int ch_base = grp * 16 * NG;
@@ -105,7 +153,10 @@ __global__ __launch_bounds__(kStreamWaves * kWave) void ffn_stream_kernel(
     if constexpr (kGateUp) sc[ng][1] = load_scale4<kScaleBf16>(S1, ch);
   }
 
-  const int nsteps = Kd >> 6;
+  // this wave's slice of the 64-wide reduction steps
+  const int nsteps_all = Kd >> 6;
+  const int s_base = kslice * nsteps_all / KS;
+  const int nsteps = (kslice + 1) * nsteps_all / KS - s_base;
 
   for (int p0 = 0; p0 < nrows; p0 += 16 * RB) {
     const int prow = min(16 * RB, nrows - p0);
@@ -124,7 +175,7 @@ __global__ __launch_bounds__(kStreamWaves * kWave) void ffn_stream_kernel(
           src = (long)(row0 + r) * Kd;
         }
       }
-      ap[rb] = X + src + 16 * lg;
+      ap[rb] = X + src + 16 * lg + (long)s_base * 64;
     }
 
     f32x4 acc[RB][NG][NMAT];
@@ -135,16 +186,23 @@ __global__ __launch_bounds__(kStreamWaves * kWave) void ffn_stream_kernel(
 #pragma unroll
         for (int m = 0; m < NMAT; ++m) acc[rb][ng][m] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+    // weights are prefetched P-1 steps ahead, activations (small, mostly
+    // L2 hits) PA-1 steps ahead; the loop body is unrolled over U steps so
+    // both ring slots are compile-time indices
+    constexpr int PA_WANT = RB >= 4 ? MOE_STREAM_PA_WIDE : P;
+    constexpr int PA = PA_WANT < P ? PA_WANT : P;
+    constexpr int U = ring_unroll(P, PA);
     uint4 bw[P][NG][NMAT];
-    bf16x8 av[P][RB][2];
+    bf16x8 av[PA][RB][2];
 
-    auto load_step = [&](int slot_unused, int s, uint4 (&b)[NG][NMAT], bf16x8 (&a)[RB][2]) {
-      (void)slot_unused;
-      const long off = (long)s * 64;
+    auto load_w = [&](int s, uint4 (&b)[NG][NMAT]) {
 #pragma unroll
       for (int ng = 0; ng < NG; ++ng)
 #pragma unroll
-        for (int m = 0; m < NMAT; ++m) b[ng][m] = load_nt16(wp[ng][m] + (long)s * 1024);
+        for (int m = 0; m < NMAT; ++m) b[ng][m] = load_nt16(wp[ng][m] + (long)(s_base + s) * 1024);
+    };
+    auto load_a = [&](int s, bf16x8 (&a)[RB][2]) {
+      const long off = (long)s * 64;
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
         if (rb < nrb && aok[rb]) {
@@ -175,17 +233,45 @@ __global__ __launch_bounds__(kStreamWaves * kWave) void ffn_stream_kernel(
 
 #pragma unroll
     for (int j = 0; j < P - 1; ++j)
-      if (j < nsteps) load_step(j, j, bw[j], av[j]);
-    for (int s0 = 0; s0 < nsteps; s0 += P) {
+      if (j < nsteps) load_w(j, bw[j]);
 #pragma unroll
-      for (int j = 0; j < P; ++j) {
+    for (int j = 0; j < PA - 1; ++j)
+      if (j < nsteps) load_a(j, av[j]);
+    for (int s0 = 0; s0 < nsteps; s0 += U) {
+#pragma unroll
+      for (int j = 0; j < U; ++j) {
         const int s = s0 + j;
-        const int sl = s + P - 1;
-        if (sl < nsteps) load_step((j + P - 1) % P, sl, bw[(j + P - 1) % P], av[(j + P - 1) % P]);
-        if (s < nsteps) compute_step(bw[j], av[j]);
+        if (s + P - 1 < nsteps) load_w(s + P - 1, bw[(j + P - 1) % P]);
+        if (s + PA - 1 < nsteps) load_a(s + PA - 1, av[(j + PA - 1) % PA]);
+        if (s < nsteps) compute_step(bw[j % P], av[j % PA]);
       }
     }
 
+    if constexpr (KS > 1) {
+      // slice 0 adds slices 1..KS-1 in order, one 16-row block at a time
+      // (nrb is the same for every wave of the workgroup)
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        if (rb < nrb) {
+          if (kslice > 0) {
+#pragma unroll
+            for (int ng = 0; ng < NG; ++ng)
+#pragma unroll
+              for (int m = 0; m < NMAT; ++m) red[kslice - 1][ng][m][lane] = acc[rb][ng][m];
+          }
+          __syncthreads();
+          if (kslice == 0) {
+            for (int j = 0; j < KS - 1; ++j)
+#pragma unroll
+              for (int ng = 0; ng < NG; ++ng)
+#pragma unroll
+                for (int m = 0; m < NMAT; ++m) acc[rb][ng][m] += red[j][ng][m][lane];
+          }
+          __syncthreads();
+        }
+      }
+      if (kslice > 0) continue;
+    }
     // ---- epilogue: lane holds channels ch_base + ng*16 + 4*lg + r, row p0 + rb*16 + li
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
@@ -213,27 +299,46 @@ __global__ __launch_bounds__(kStreamWaves * kWave) void ffn_stream_kernel(
   }
 }
 
-template <bool kGateUp, typename Act, bool kScaleBf16>
-hipError_t launch_stream_pass(const FfnArgs& a, hipStream_t stream) {
-  constexpr int NG = kGateUp ? MOE_STREAM_NG_GU : MOE_STREAM_NG_DN;
+template <bool kGateUp, typename Act, bool kScaleBf16, int RB, int KS>
+hipError_t launch_stream_pass_ks(const FfnArgs& a, long items, hipStream_t stream) {
+  constexpr int NG = kGateUp ? MOE_STREAM_NG_GU : (RB >= 4 ? MOE_STREAM_NG_DN_WIDE : MOE_STREAM_NG_DN);
   constexpr int P = kGateUp ? MOE_STREAM_P_GU : MOE_STREAM_P_DN;
-  constexpr int RB = MOE_STREAM_RB;
   const int N = kGateUp ? a.f : a.d;
   const int Kd = kGateUp ? a.d : a.f;
-  const int gpe = N / (16 * NG);
-  const long items = (long)a.E * gpe;
-  const dim3 grid((unsigned)((items + kStreamWaves - 1) / kStreamWaves));
-  const dim3 block(kStreamWaves * kWave);
+  const dim3 grid((unsigned)(KS > 1 ? items : (items + kStreamWaves - 1) / kStreamWaves));
+  const dim3 block(stream_block_waves(KS) * kWave);
   if constexpr (kGateUp) {
-    hipLaunchKernelGGL((ffn_stream_kernel<true, Act, kScaleBf16, NG, RB, P>), grid, block, 0, stream,
+    hipLaunchKernelGGL((ffn_stream_kernel<true, Act, kScaleBf16, NG, RB, P, KS>), grid, block, 0, stream,
                        static_cast<const Act*>(a.x), a.sorted_slots, a.K, a.w_gate, a.w_up, a.s_gate, a.s_up,
                        a.offsets, a.E, N, Kd, static_cast<void*>(a.h));
   } else {
-    hipLaunchKernelGGL((ffn_stream_kernel<false, __bf16, kScaleBf16, NG, RB, P>), grid, block, 0, stream,
+    hipLaunchKernelGGL((ffn_stream_kernel<false, __bf16, kScaleBf16, NG, RB, P, KS>), grid, block, 0, stream,
                        static_cast<const __bf16*>(a.h), a.sorted_slots, a.K, a.w_down, nullptr, a.s_down,
                        nullptr, a.offsets, a.E, N, Kd, static_cast<void*>(a.y_rows));
   }
   return hipGetLastError();
+}
+
+template <bool kGateUp, typename Act, bool kScaleBf16, int RB>
+hipError_t launch_stream_pass_rb(const FfnArgs& a, hipStream_t stream) {
+  constexpr int NG = kGateUp ? MOE_STREAM_NG_GU : (RB >= 4 ? MOE_STREAM_NG_DN_WIDE : MOE_STREAM_NG_DN);
+  const int N = kGateUp ? a.f : a.d;
+  const long items = (long)a.E * (N / (16 * NG));
+  switch (choose_split(items, RB)) {
+    case 1: return launch_stream_pass_ks<kGateUp, Act, kScaleBf16, RB, 1>(a, items, stream);
+    case 2: return launch_stream_pass_ks<kGateUp, Act, kScaleBf16, RB, 2>(a, items, stream);
+    case 4: return launch_stream_pass_ks<kGateUp, Act, kScaleBf16, RB, 4>(a, items, stream);
+    default: return launch_stream_pass_ks<kGateUp, Act, kScaleBf16, RB, 8>(a, items, stream);
+  }
+}
+
+// Rows per pass: 16*RB. More than 32 rows per expert on average (a dense MLP
+// layer, or a hot expert at decode) takes the 64-row variant so the weights
+// are streamed once; otherwise the 32-row variant keeps more waves resident.
+template <bool kGateUp, typename Act, bool kScaleBf16>
+hipError_t launch_stream_pass(const FfnArgs& a, hipStream_t stream) {
+  if ((long)a.S > 32L * a.E) return launch_stream_pass_rb<kGateUp, Act, kScaleBf16, 4>(a, stream);
+  return launch_stream_pass_rb<kGateUp, Act, kScaleBf16, MOE_STREAM_RB>(a, stream);
 }
 
 template <bool kGateUp>

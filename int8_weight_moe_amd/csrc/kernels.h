@@ -43,6 +43,9 @@ hipError_t launch_tiled_down(const FfnArgs& a, hipStream_t stream);
 hipError_t launch_combine(const float* y_rows, const int32_t* slot_to_row, const float* topk_w, int T, int d,
                           int K, bool act_bf16, void* y, hipStream_t stream);
 
+hipError_t launch_dense_init(int T, int32_t* offsets, int32_t* sorted_slots, int32_t* slot_to_row, float* w,
+                             hipStream_t stream);
+
 hipError_t launch_pack_rows(long rows, int cols, const int8_t* src, int8_t* dst, hipStream_t stream);
 
 hipError_t launch_quantize_rows(int64_t rows, int cols, bool src_bf16, const void* w, bool scale_bf16, int8_t* q,

@@ -228,6 +228,27 @@ def moe_forward(x: torch.Tensor, router_w: torch.Tensor, bias: Optional[torch.Te
     return y, ids, w
 
 
+def moe_mlp_forward(x: torch.Tensor, experts: Int8Experts, path: int = MOE_PATH_AUTO,
+                    y: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Dense int8-weight SwiGLU MLP (one expert, E = K = 1). Returns y [T, d] in x.dtype."""
+    lib = _lib_handle()
+    T, d = x.shape
+    if experts.E != 1:
+        raise ValueError("the dense MLP takes one expert (E = 1)")
+    shape = make_shape(T, d, experts.f, 1, 1, x.dtype, experts.scale_dtype, path)
+    if y is None:
+        y = torch.empty((T, d), dtype=x.dtype, device=x.device)
+    if workspace is None:
+        n = ctypes.c_size_t(0)
+        _lib.check(lib.moe_mlp_workspace_size(ctypes.byref(shape), ctypes.byref(n)))
+        workspace = torch.empty(max(n.value, 256), dtype=torch.uint8, device=x.device)
+    _lib.check(lib.moe_mlp_forward(
+        ctypes.byref(shape), _ptr(x), _ptr(experts.q_gate), _ptr(experts.q_up), _ptr(experts.q_down),
+        _ptr(experts.s_gate), _ptr(experts.s_up), _ptr(experts.s_down), _ptr(y), _ptr(workspace),
+        ctypes.c_size_t(workspace.numel()), _stream()))
+    return y
+
+
 def moe_quantize_rows(w: torch.Tensor, scale_dtype: torch.dtype):
     """ExpertsInt8 quantizer on the GPU: w [..., cols] (fp32/bf16) -> (q int8 [..., cols], s [...])."""
     lib = _lib_handle()

@@ -120,6 +120,17 @@ def test_empty_input_enqueues_nothing(lib):
                            ctypes.c_size_t(need.value), None) == 0
 
 
+def test_mlp_validation(lib):
+    s = _shape(E=2, K=1)
+    n = ctypes.c_size_t(0)
+    assert lib.moe_mlp_workspace_size(ctypes.byref(s), ctypes.byref(n)) == 2
+    assert lib.moe_mlp_forward(ctypes.byref(s), A, A, A, A, A, A, A, A, A, ctypes.c_size_t(1 << 30), None) == 2
+    s = _shape(E=1, K=1)
+    assert lib.moe_mlp_workspace_size(ctypes.byref(s), ctypes.byref(n)) == 0
+    assert lib.moe_mlp_forward(ctypes.byref(s), A, A, A, A, A, A, None, A, A, ctypes.c_size_t(1 << 30), None) == 1
+    assert lib.moe_mlp_forward(ctypes.byref(s), A, A, A, A, A, A, A, A, A, ctypes.c_size_t(n.value - 1), None) == 5
+
+
 def test_pack_validation(lib):
     assert lib.moe_pack_rows(8, 64, A, B, None) == 2        # rows % 16
     assert lib.moe_pack_rows(16, 96, A, B, None) == 2       # cols % 64

@@ -65,6 +65,13 @@ LARGE_PREFILL_SKEWED = Workload("large-prefill-skewed", T=16384, d=8192, f=24576
 
 WORKLOADS = {w.name: w for w in (TINY, MINI_DECODE, MINI_PREFILL, LARGE_DECODE, LARGE_PREFILL_SKEWED)}
 
+# Dense MLP layers of the same model (ExpertsInt8 covers them too): one expert,
+# every token, no router. Their FFN width is taken equal to the experts'.
+LARGE_MLP_DECODE = Workload("large-mlp-decode", T=64, d=8192, f=24576, E=1, K=1)
+LARGE_MLP_PREFILL = Workload("large-mlp-prefill", T=8192, d=8192, f=24576, E=1, K=1)
+DENSE_WORKLOADS = {w.name: w for w in (LARGE_MLP_DECODE, LARGE_MLP_PREFILL)}
+ALL_WORKLOADS = {**WORKLOADS, **DENSE_WORKLOADS}
+
 TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}
 
 # stream ids inside the SeedSequence spawn
