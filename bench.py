@@ -47,6 +47,8 @@ def parse():
     ap.add_argument("--prefill-steps", type=int, default=10)
     ap.add_argument("--no-prefill", action="store_true", help="skip the sibling prefill workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-compare", action="store_true",
+                    help="skip the weight-encoding comparators (the same layer with bf16 weights)")
     ap.add_argument("--cpu-sample-experts", type=int, default=4)
     ap.add_argument("--path", choices=["auto", "stream", "tiled"], default="auto")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -85,16 +87,20 @@ def touched_rows(layer, x, path):
     return [o[i + 1] - o[i] for i in range(len(o) - 1)]
 
 
-def algorithmic(w, counts):
-    """Bytes and flops the layer (and each contraction kernel) must move / compute."""
+def algorithmic(w, counts, wfmt="int8"):
+    """Bytes and flops the layer (and each contraction kernel) must move / compute.
+
+    wfmt: weight encoding -- int8 (1 byte per weight plus per-channel scales) or
+    bf16 (2 bytes per weight, no scales)."""
     ab = 4 if w.act == "f32" else 2
-    sb = 4 if w.scale == "f32" else 2
+    wb = 2 if wfmt == "bf16" else 1
+    sb = 0 if wfmt == "bf16" else (4 if w.scale == "f32" else 2)
     touched = sum(1 for c in counts if c > 0)
     S = w.T * w.K
     d, f = w.d, w.f
-    gate_up_bytes = touched * (2 * d * f + 2 * f * sb) + w.T * d * ab + S * f * 2
-    down_bytes = touched * (d * f + d * sb) + S * f * 2 + S * d * 4
-    layer_bytes = touched * (3 * d * f + (2 * f + d) * sb) + 2 * w.T * d * ab + w.E * d * ab
+    gate_up_bytes = touched * (2 * d * f * wb + 2 * f * sb) + w.T * d * ab + S * f * 2
+    down_bytes = touched * (d * f * wb + d * sb) + S * f * 2 + S * d * 4
+    layer_bytes = touched * (3 * d * f * wb + (2 * f + d) * sb) + 2 * w.T * d * ab + w.E * d * ab
     return {
         "touched": touched,
         "gate_up_bytes": gate_up_bytes, "down_bytes": down_bytes, "layer_bytes": layer_bytes,
@@ -283,6 +289,32 @@ def cpu_baseline(w, x_host, layer, src, n_experts):
             "step_ms_estimate": round(est * 1e3, 1)}
 
 
+def measure_prefill(layer, wp, xp, bias, args, dense, wfmt="int8"):
+    """Step time, kernel split and roofline of the sibling prefill workload on this layer."""
+    from int8_weight_moe_amd._lib import MOE_PATH_AUTO
+    orig_bias = layer.bias
+    if bias is not None:
+        layer.bias = bias
+    cp = touched_rows(layer, xp, MOE_PATH_AUTO)
+    ap_ = algorithmic(wp, cp, wfmt)
+    pms, _ = time_forward(layer, xp, MOE_PATH_AUTO, args.prefill_steps, 2, dense)
+    pst = time_stages(layer, xp, MOE_PATH_AUTO, max(3, args.prefill_steps // 2), 1, dense)
+    layer.bias = orig_bias
+    pdom = max(("gate_up", "down"), key=lambda k: pst[k])
+    log(f"prefill {wp.name} ({wfmt} weights): {pms:.3f} ms/step; stages (us): "
+        + ", ".join(f"{k}={v:.1f}" for k, v in pst.items()))
+    out = {
+        "workload": wp.name, "T": wp.T, "ms_per_step": round(pms, 4),
+        "tokens_per_s": round(wp.T / (pms * 1e-3), 1),
+        "layer_tflops": round(ap_["layer_flops"] / (pms * 1e-3) / 1e12, 1),
+        "layer_mfma_frac": round(ap_["layer_flops"] / (pms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+        "kernels_us": {k: round(v, 2) for k, v in pst.items()},
+    }
+    if wfmt == "int8":
+        out["roofline"] = roofline(wp, ap_, pst, pdom, wp.name, ffn_path_used(wp, MOE_PATH_AUTO) == "stream")
+    return out
+
+
 # ----------------------------------------------------------------------------- main
 def main():
     args = parse()
@@ -340,31 +372,46 @@ def main():
         "quantize_ms": round(qms, 2),
     }
 
+    # the sibling prefill workload of the same layer (same weights)
+    prefill_x, prefill_bias = None, None
     sib = SIBLING.get(w.name)
     if sib and not args.no_prefill:
         wp = workloads.ALL_WORKLOADS[sib]
         if (wp.d, wp.f, wp.E) == (w.d, w.f, w.E):
-            orig_bias = layer.bias
+            prefill_x = workloads.draw_activations(wp).to(dev)
             if wp.has_bias:
-                layer.bias = torch.tensor([wp.hot_bias, wp.hot_bias] + [0.0] * (w.E - 2), device=dev)
-            xp = workloads.draw_activations(wp).to(dev)
-            cp = touched_rows(layer, xp, MOE_PATH_AUTO)
-            ap_ = algorithmic(wp, cp)
-            pms, _ = time_forward(layer, xp, MOE_PATH_AUTO, args.prefill_steps, 2, dense)
-            pst = time_stages(layer, xp, MOE_PATH_AUTO, max(3, args.prefill_steps // 2), 1, dense)
-            pdom = max(("gate_up", "down"), key=lambda k: pst[k])
-            log(f"prefill {wp.name}: {pms:.3f} ms/step; stages (us): "
-                + ", ".join(f"{k}={v:.1f}" for k, v in pst.items()))
-            result["prefill"] = {
-                "workload": wp.name, "T": wp.T, "ms_per_step": round(pms, 4),
-                "tokens_per_s": round(wp.T / (pms * 1e-3), 1),
-                "layer_tflops": round(ap_["layer_flops"] / (pms * 1e-3) / 1e12, 1),
-                "layer_mfma_frac": round(ap_["layer_flops"] / (pms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
-                "roofline": roofline(wp, ap_, pst, pdom, wp.name, ffn_path_used(wp, MOE_PATH_AUTO) == "stream"),
-                "kernels_us": {k: round(v, 2) for k, v in pst.items()},
-            }
-            layer.bias = orig_bias
-            del xp
+                prefill_bias = torch.tensor([wp.hot_bias, wp.hot_bias] + [0.0] * (w.E - 2), device=dev)
+            result["prefill"] = measure_prefill(layer, wp, prefill_x, prefill_bias, args, dense)
+
+    # weight-encoding comparators: the same layer, inputs and schedule choice
+    if not args.no_compare and w.act == "bf16" and w.weight_src == "bf16":
+        from int8_weight_moe_amd import MoeLayer, pack_bf16_experts
+        comp = {}
+        for name in ("bf16",):
+            ex = pack_bf16_experts(src["w_gate"], src["w_up"], src["w_down"])
+            clayer = MoeLayer(layer.router_w, layer.bias, ex, w.K)
+            cms, _ = time_forward(clayer, x, path, args.steps, args.warmup, dense)
+            cst = time_stages(clayer, x, path, args.steps, args.warmup, dense)
+            calg = algorithmic(w, counts, wfmt=name)
+            log(f"{name} weights: {cms * 1e3:.1f} us/step; stages (us): "
+                + ", ".join(f"{k}={v:.1f}" for k, v in cst.items()))
+            entry = {"weights": "bf16 as stored, no scales" if name == "bf16" else name,
+                     "ms_per_step": round(cms, 4), "tokens_per_s": round(w.T / (cms * 1e-3), 1),
+                     "int8_speedup": round(cms / ms, 3),
+                     "layer_GB": round(calg["layer_bytes"] / 1e9, 4),
+                     "hbm_GBps": round(calg["layer_bytes"] / (cms * 1e-3) / 1e9, 1),
+                     "kernels_us": {k: round(v, 2) for k, v in cst.items()}}
+            if prefill_x is not None:
+                wp = workloads.ALL_WORKLOADS[sib]
+                pr = measure_prefill(clayer, wp, prefill_x, prefill_bias, args, dense, wfmt=name)
+                entry["prefill"] = {"workload": wp.name, "ms_per_step": pr["ms_per_step"],
+                                    "int8_speedup": round(pr["ms_per_step"] / result["prefill"]["ms_per_step"], 3),
+                                    "kernels_us": pr["kernels_us"]}
+            comp[name + "_weights"] = entry
+            del ex, clayer
+            torch.cuda.empty_cache()
+        result["comparators"] = comp
+    del prefill_x
 
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib << 20

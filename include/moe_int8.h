@@ -35,9 +35,10 @@
  *     reported by HIP maps to MOE_ERR_HIP. Device-side faults surface at the
  *     caller's next synchronisation.
  *   - Expert weights are (out, in) matrices w_gate, w_up [E, f, d] and
- *     w_down [E, d, f], held by the FFN calls in the TILED INT8 LAYOUT that
- *     moe_pack_rows produces (see there). router_w [E, d] is row-major;
- *     scales s_gate, s_up [E, f], s_down [E, d] are row-major.
+ *     w_down [E, d, f] in the encoding shape->weight_fmt names (int8 unless
+ *     stated), held by the FFN calls in the TILED LAYOUT that moe_pack_rows
+ *     produces (see there). router_w [E, d] is row-major; scales
+ *     s_gate, s_up [E, f], s_down [E, d] are row-major.
  *   - Slots: token t's k-th choice is slot s = t*K + k.
  *   - T = 0 is valid and enqueues nothing.
  */
@@ -67,6 +68,21 @@ enum {
 /* dtype codes */
 enum { MOE_F32 = 0, MOE_BF16 = 1 };
 
+/* Expert weight encodings (moe_shape.weight_fmt). MOE_W_INT8 is the layer
+ * itself (ExpertsInt8). The other two are comparators for the paper's claims
+ * ("Serving Considerations and Improvements": in-kernel INT8 dequantization is
+ * faster than BF16 weights and as fast as FP8):
+ *   MOE_W_INT8  int8 codes + per-output-channel scales (moe_quantize_rows);
+ *   MOE_W_BF16  the bf16 weights themselves, no scales (s_* unused, may be NULL);
+ *   MOE_W_FP8   OCP fp8 e4m3 codes + per-output-channel scales
+ *               (moe_quantize_rows_fp8); every e4m3 value is exact in bf16.
+ * All three are held in the tiled layout of their bytes (moe_pack_rows; a
+ * bf16 matrix [rows, cols] is packed as int8 [rows, 2*cols]). The bf16 and
+ * fp8 encodings need bf16 activations; on the TILED schedule their tensors
+ * must also fit 32-bit byte offsets (x and h below 4 GiB, one expert's matrix
+ * below 4 GiB), else MOE_ERR_UNSUPPORTED. */
+enum { MOE_W_INT8 = 0, MOE_W_BF16 = 1, MOE_W_FP8 = 2 };
+
 /* expert-FFN schedule: AUTO picks STREAM when at most 64 rows fall on each
  * expert on average (T*K <= 64*E: decode) and TILED otherwise (prefill).
  * Both give results within the same tolerance of the exact layer; they are
@@ -82,10 +98,11 @@ typedef struct moe_shape {
   int32_t act_dtype;   /* x, router_w, y: MOE_F32 or MOE_BF16               */
   int32_t scale_dtype; /* s_gate, s_up, s_down: MOE_F32 or MOE_BF16         */
   int32_t ffn_path;    /* MOE_PATH_*                                        */
+  int32_t weight_fmt;  /* MOE_W_*: encoding of w_gate, w_up, w_down        */
 } moe_shape;
 
 /* ABI version of this header (bumped on any signature change). */
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 int32_t moe_abi_version(void);
 
 /* Static description of a status code. */
@@ -133,7 +150,7 @@ moe_status moe_permute(const moe_shape* shape, const int32_t* topk_ids,
  * Rows past off[E] are left untouched. */
 moe_status moe_expert_ffn(const moe_shape* shape, const void* x,
                           const int32_t* expert_offsets, const int32_t* sorted_slots,
-                          const int8_t* w_gate, const int8_t* w_up, const int8_t* w_down,
+                          const void* w_gate, const void* w_up, const void* w_down,
                           const void* s_gate, const void* s_up, const void* s_down,
                           float* y_rows, void* workspace, size_t workspace_bytes,
                           hipStream_t stream);
@@ -144,10 +161,10 @@ moe_status moe_expert_ffn(const moe_shape* shape, const void* x,
  * down     y_rows[r] = s_d * (q_d . h[r]),  h [T*K, f] bf16 in, y_rows [T*K, d] fp32 out.
  * moe_expert_ffn is moe_expert_gate_up followed by moe_expert_down on the same stream. */
 moe_status moe_expert_gate_up(const moe_shape* shape, const void* x, const int32_t* expert_offsets,
-                              const int32_t* sorted_slots, const int8_t* w_gate, const int8_t* w_up,
+                              const int32_t* sorted_slots, const void* w_gate, const void* w_up,
                               const void* s_gate, const void* s_up, void* h, hipStream_t stream);
 moe_status moe_expert_down(const moe_shape* shape, const void* h, const int32_t* expert_offsets,
-                           const int8_t* w_down, const void* s_down, float* y_rows, hipStream_t stream);
+                           const void* w_down, const void* s_down, float* y_rows, hipStream_t stream);
 
 /* Weighted combine back to token order: y[t] = sum_k topk_w[t,k] * y_rows[slot_to_row[t*K+k]]
  * (k ascending, fp32, no atomics); a slot with row -1 contributes nothing.
@@ -161,7 +178,7 @@ moe_status moe_combine(const moe_shape* shape, const float* y_rows, const int32_
  *   workspace    >= moe_workspace_size bytes */
 moe_status moe_forward(const moe_shape* shape, const void* x, const void* router_w,
                        const float* router_bias,
-                       const int8_t* w_gate, const int8_t* w_up, const int8_t* w_down,
+                       const void* w_gate, const void* w_up, const void* w_down,
                        const void* s_gate, const void* s_up, const void* s_down,
                        void* y, int32_t* topk_ids_out, float* topk_w_out,
                        void* workspace, size_t workspace_bytes, hipStream_t stream);
@@ -175,7 +192,7 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const void* router
  *   y [T, d] act_dtype out; workspace >= moe_mlp_workspace_size bytes. */
 moe_status moe_mlp_workspace_size(const moe_shape* shape, size_t* bytes);
 moe_status moe_mlp_forward(const moe_shape* shape, const void* x,
-                           const int8_t* w_gate, const int8_t* w_up, const int8_t* w_down,
+                           const void* w_gate, const void* w_up, const void* w_down,
                            const void* s_gate, const void* s_up, const void* s_down, void* y,
                            void* workspace, size_t workspace_bytes, hipStream_t stream);
 

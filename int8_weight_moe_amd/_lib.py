@@ -11,7 +11,7 @@ import os
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libmoe_int8.so")
 
-ABI_VERSION = 2
+ABI_VERSION = 3
 MOE_OK = 0
 STATUS_NAMES = {
     0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_DTYPE", 4: "MOE_ERR_ALIGN",
@@ -19,6 +19,7 @@ STATUS_NAMES = {
 }
 MOE_F32, MOE_BF16 = 0, 1
 MOE_PATH_AUTO, MOE_PATH_STREAM, MOE_PATH_TILED = 0, 1, 2
+MOE_W_INT8, MOE_W_BF16, MOE_W_FP8 = 0, 1, 2
 
 # every symbol the header declares
 EXPORTS = (
@@ -31,7 +32,7 @@ EXPORTS = (
 class MoeShape(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int32), ("d", ctypes.c_int32), ("f", ctypes.c_int32), ("E", ctypes.c_int32),
                 ("K", ctypes.c_int32), ("act_dtype", ctypes.c_int32), ("scale_dtype", ctypes.c_int32),
-                ("ffn_path", ctypes.c_int32)]
+                ("ffn_path", ctypes.c_int32), ("weight_fmt", ctypes.c_int32)]
 
 
 class MoeError(RuntimeError):

@@ -45,6 +45,7 @@ moe_status check_shape(const moe_shape* s) {
   if (s->act_dtype != MOE_F32 && s->act_dtype != MOE_BF16) return fail(MOE_ERR_DTYPE, "act_dtype=%d", s->act_dtype);
   if (s->scale_dtype != MOE_F32 && s->scale_dtype != MOE_BF16) return fail(MOE_ERR_DTYPE, "scale_dtype=%d", s->scale_dtype);
   if (s->ffn_path < MOE_PATH_AUTO || s->ffn_path > MOE_PATH_TILED) return fail(MOE_ERR_SHAPE, "ffn_path=%d", s->ffn_path);
+  if (s->weight_fmt < MOE_W_INT8 || s->weight_fmt > MOE_W_FP8) return fail(MOE_ERR_DTYPE, "weight_fmt=%d", s->weight_fmt);
   return MOE_OK;
 }
 
@@ -52,6 +53,12 @@ moe_status check_shape(const moe_shape* s) {
   do {                                                                         \
     if (!(p)) return fail(MOE_ERR_NULL, "%s is NULL", #p);                     \
     if (!aligned16(p)) return fail(MOE_ERR_ALIGN, "%s is not 16-byte aligned", #p); \
+  } while (0)
+
+// Scales are read for the scaled weight encodings (int8, fp8) only.
+#define REQUIRE_SCALE(s, p)                                                    \
+  do {                                                                         \
+    if ((s)->weight_fmt != MOE_W_BF16) REQUIRE_PTR(p);                         \
   } while (0)
 
 struct WsLayout {
@@ -81,8 +88,21 @@ bool use_stream(const moe_shape* s) {
   return (long)s->T * s->K <= kStreamRowsPerExpert * s->E;
 }
 
+// What the FFN kernels accept beyond check_shape: the bf16 and fp8 weight
+// encodings run with bf16 activations, and their tiled schedule addresses
+// with 32-bit offsets.
+moe_status check_ffn(const moe_shape* s) {
+  if (s->weight_fmt == MOE_W_INT8) return MOE_OK;
+  if (s->act_dtype != MOE_BF16)
+    return fail(MOE_ERR_UNSUPPORTED, "weight_fmt=%d needs bf16 activations", s->weight_fmt);
+  const int wbytes = s->weight_fmt == MOE_W_BF16 ? 2 : 1;
+  if (!use_stream(s) && !moe::dma_offsets_fit(s->T, (long)s->T * s->K, s->d, s->f, wbytes))
+    return fail(MOE_ERR_UNSUPPORTED, "weight_fmt=%d: tensors too large for the tiled schedule", s->weight_fmt);
+  return MOE_OK;
+}
+
 moe::FfnArgs ffn_args(const moe_shape* s, const void* x, const int32_t* offsets, const int32_t* sorted_slots,
-                      const int8_t* w_gate, const int8_t* w_up, const int8_t* w_down, const void* s_gate,
+                      const void* w_gate, const void* w_up, const void* w_down, const void* s_gate,
                       const void* s_up, const void* s_down, float* y_rows, __bf16* h) {
   moe::FfnArgs a;
   a.x = x;
@@ -90,9 +110,10 @@ moe::FfnArgs ffn_args(const moe_shape* s, const void* x, const int32_t* offsets,
   a.scale_bf16 = s->scale_dtype == MOE_BF16;
   a.offsets = offsets;
   a.sorted_slots = sorted_slots;
-  a.w_gate = w_gate;
-  a.w_up = w_up;
-  a.w_down = w_down;
+  a.wfmt = s->weight_fmt;
+  a.w_gate = static_cast<const int8_t*>(w_gate);
+  a.w_up = static_cast<const int8_t*>(w_up);
+  a.w_down = static_cast<const int8_t*>(w_down);
   a.s_gate = s_gate;
   a.s_up = s_up;
   a.s_down = s_down;
@@ -189,10 +210,12 @@ moe_status moe_permute(const moe_shape* s, const int32_t* topk_ids, int32_t* exp
 }
 
 moe_status moe_expert_ffn(const moe_shape* s, const void* x, const int32_t* expert_offsets,
-                          const int32_t* sorted_slots, const int8_t* w_gate, const int8_t* w_up,
-                          const int8_t* w_down, const void* s_gate, const void* s_up, const void* s_down,
+                          const int32_t* sorted_slots, const void* w_gate, const void* w_up,
+                          const void* w_down, const void* s_gate, const void* s_up, const void* s_down,
                           float* y_rows, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  st = check_ffn(s);
   if (st != MOE_OK) return st;
   REQUIRE_PTR(x);
   REQUIRE_PTR(expert_offsets);
@@ -200,9 +223,9 @@ moe_status moe_expert_ffn(const moe_shape* s, const void* x, const int32_t* expe
   REQUIRE_PTR(w_gate);
   REQUIRE_PTR(w_up);
   REQUIRE_PTR(w_down);
-  REQUIRE_PTR(s_gate);
-  REQUIRE_PTR(s_up);
-  REQUIRE_PTR(s_down);
+  REQUIRE_SCALE(s, s_gate);
+  REQUIRE_SCALE(s, s_up);
+  REQUIRE_SCALE(s, s_down);
   REQUIRE_PTR(y_rows);
   REQUIRE_PTR(workspace);
   const size_t need = ffn_ws_bytes(s);
@@ -217,17 +240,19 @@ moe_status moe_expert_ffn(const moe_shape* s, const void* x, const int32_t* expe
 }
 
 moe_status moe_expert_gate_up(const moe_shape* s, const void* x, const int32_t* expert_offsets,
-                              const int32_t* sorted_slots, const int8_t* w_gate, const int8_t* w_up,
+                              const int32_t* sorted_slots, const void* w_gate, const void* w_up,
                               const void* s_gate, const void* s_up, void* h, hipStream_t stream) {
   moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  st = check_ffn(s);
   if (st != MOE_OK) return st;
   REQUIRE_PTR(x);
   REQUIRE_PTR(expert_offsets);
   REQUIRE_PTR(sorted_slots);
   REQUIRE_PTR(w_gate);
   REQUIRE_PTR(w_up);
-  REQUIRE_PTR(s_gate);
-  REQUIRE_PTR(s_up);
+  REQUIRE_SCALE(s, s_gate);
+  REQUIRE_SCALE(s, s_up);
   REQUIRE_PTR(h);
   if (s->T == 0) return MOE_OK;
   const moe::FfnArgs a = ffn_args(s, x, expert_offsets, sorted_slots, w_gate, w_up, nullptr, s_gate, s_up, nullptr,
@@ -235,14 +260,16 @@ moe_status moe_expert_gate_up(const moe_shape* s, const void* x, const int32_t* 
   return run_gate_up(s, a, stream);
 }
 
-moe_status moe_expert_down(const moe_shape* s, const void* h, const int32_t* expert_offsets, const int8_t* w_down,
+moe_status moe_expert_down(const moe_shape* s, const void* h, const int32_t* expert_offsets, const void* w_down,
                            const void* s_down, float* y_rows, hipStream_t stream) {
   moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  st = check_ffn(s);
   if (st != MOE_OK) return st;
   REQUIRE_PTR(h);
   REQUIRE_PTR(expert_offsets);
   REQUIRE_PTR(w_down);
-  REQUIRE_PTR(s_down);
+  REQUIRE_SCALE(s, s_down);
   REQUIRE_PTR(y_rows);
   if (s->T == 0) return MOE_OK;
   const moe::FfnArgs a = ffn_args(s, nullptr, expert_offsets, nullptr, nullptr, nullptr, w_down, nullptr, nullptr,
@@ -266,19 +293,21 @@ moe_status moe_combine(const moe_shape* s, const float* y_rows, const int32_t* s
 }
 
 moe_status moe_forward(const moe_shape* s, const void* x, const void* router_w, const float* router_bias,
-                       const int8_t* w_gate, const int8_t* w_up, const int8_t* w_down, const void* s_gate,
+                       const void* w_gate, const void* w_up, const void* w_down, const void* s_gate,
                        const void* s_up, const void* s_down, void* y, int32_t* topk_ids_out, float* topk_w_out,
                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
   moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  st = check_ffn(s);
   if (st != MOE_OK) return st;
   REQUIRE_PTR(x);
   REQUIRE_PTR(router_w);
   REQUIRE_PTR(w_gate);
   REQUIRE_PTR(w_up);
   REQUIRE_PTR(w_down);
-  REQUIRE_PTR(s_gate);
-  REQUIRE_PTR(s_up);
-  REQUIRE_PTR(s_down);
+  REQUIRE_SCALE(s, s_gate);
+  REQUIRE_SCALE(s, s_up);
+  REQUIRE_SCALE(s, s_down);
   REQUIRE_PTR(y);
   REQUIRE_PTR(workspace);
   if (router_bias && !aligned16(router_bias)) return fail(MOE_ERR_ALIGN, "router_bias is not 16-byte aligned");
@@ -322,19 +351,21 @@ moe_status moe_mlp_workspace_size(const moe_shape* shape, size_t* bytes) {
   return MOE_OK;
 }
 
-moe_status moe_mlp_forward(const moe_shape* s, const void* x, const int8_t* w_gate, const int8_t* w_up,
-                           const int8_t* w_down, const void* s_gate, const void* s_up, const void* s_down, void* y,
+moe_status moe_mlp_forward(const moe_shape* s, const void* x, const void* w_gate, const void* w_up,
+                           const void* w_down, const void* s_gate, const void* s_up, const void* s_down, void* y,
                            void* workspace, size_t workspace_bytes, hipStream_t stream) {
   moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  st = check_ffn(s);
   if (st != MOE_OK) return st;
   if (s->E != 1 || s->K != 1) return fail(MOE_ERR_SHAPE, "the dense MLP needs E = K = 1 (E=%d, K=%d)", s->E, s->K);
   REQUIRE_PTR(x);
   REQUIRE_PTR(w_gate);
   REQUIRE_PTR(w_up);
   REQUIRE_PTR(w_down);
-  REQUIRE_PTR(s_gate);
-  REQUIRE_PTR(s_up);
-  REQUIRE_PTR(s_down);
+  REQUIRE_SCALE(s, s_gate);
+  REQUIRE_SCALE(s, s_up);
+  REQUIRE_SCALE(s, s_down);
   REQUIRE_PTR(y);
   REQUIRE_PTR(workspace);
   const WsLayout L = forward_layout(s);

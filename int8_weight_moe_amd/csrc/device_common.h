@@ -120,4 +120,87 @@ __device__ __forceinline__ bf16x8 zero_bf16x8() {
   return as_bf16x8(make_uint4(0, 0, 0, 0));
 }
 
+// Eight consecutive activations starting at p, as bf16x8.
+__device__ __forceinline__ bf16x8 load_act8(const __bf16* p) {
+  return as_bf16x8(*reinterpret_cast<const uint4*>(p));
+}
+__device__ __forceinline__ bf16x8 load_act8(const float* p) {
+  const float4* q = reinterpret_cast<const float4*>(p);
+  return f32x8_to_bf16(q[0], q[1]);
+}
+
+// ---------------------------------------------------------------- weight encodings
+// The FFN kernels read expert weights in the tiled layout of their bytes (the
+// layout moe_pack_rows makes, applied to a row of 2*cols bytes for bf16): per
+// 16-channel group and 64-wide reduction step a wave reads kPieces 1 KiB blocks,
+// lane l taking the 16 bytes at 16*l of each (channel l%16). Each encoding
+// turns a lane's pieces into the two bf16x8 MFMA operands of the step and says
+// which reduction elements they hold: operand 0 holds elements
+// kActLane*(l/16) + 0..7 of the step, operand 1 the same plus kActSecond.
+enum WFmt : int { kWInt8 = 0, kWBf16 = 1, kWFp8 = 2 };
+
+template <int F>
+struct WFormat;
+
+// int8 codes (ExpertsInt8), one scale per output channel. Byte j of a piece is
+// reduction element 16*(l/16) + j.
+template <>
+struct WFormat<kWInt8> {
+  static constexpr int kPieces = 1;
+  static constexpr bool kScaled = true;
+  static constexpr int kActLane = 16;
+  static constexpr int kActSecond = 8;
+  static __device__ __forceinline__ bf16x8 operand(const uint4 (&p)[1], int k) {
+    return k == 0 ? i8x8_to_bf16(p[0].x, p[0].y) : i8x8_to_bf16(p[0].z, p[0].w);
+  }
+  static __device__ __forceinline__ void operands(const uint4 (&p)[1], bf16x8& w0, bf16x8& w1) {
+    w0 = operand(p, 0);
+    w1 = operand(p, 1);
+  }
+};
+
+// bf16 weights as they are (the comparator without quantization): two pieces
+// per step, piece h holding elements 32*h + 8*(l/16) + 0..7.
+template <>
+struct WFormat<kWBf16> {
+  static constexpr int kPieces = 2;
+  static constexpr bool kScaled = false;
+  static constexpr int kActLane = 8;
+  static constexpr int kActSecond = 32;
+  static __device__ __forceinline__ bf16x8 operand(const uint4 (&p)[2], int k) { return as_bf16x8(p[k]); }
+  static __device__ __forceinline__ void operands(const uint4 (&p)[2], bf16x8& w0, bf16x8& w1) {
+    w0 = as_bf16x8(p[0]);
+    w1 = as_bf16x8(p[1]);
+  }
+};
+
+// OCP fp8 e4m3 codes, one scale per output channel; byte order as int8. Every
+// e4m3 value is exact in bf16 (3 mantissa bits, exponents 2^-9..2^8), so the
+// gfx950 packed convert with a unit scale is exact.
+template <>
+struct WFormat<kWFp8> {
+  static constexpr int kPieces = 1;
+  static constexpr bool kScaled = true;
+  static constexpr int kActLane = 16;
+  static constexpr int kActSecond = 8;
+  static __device__ __forceinline__ bf16x8 fp8x8(uint32_t lo, uint32_t hi) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
+    const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
+    const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+    const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
+    bf16x8 r;
+    r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
+    r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
+    return r;
+  }
+  static __device__ __forceinline__ bf16x8 operand(const uint4 (&p)[1], int k) {
+    return k == 0 ? fp8x8(p[0].x, p[0].y) : fp8x8(p[0].z, p[0].w);
+  }
+  static __device__ __forceinline__ void operands(const uint4 (&p)[1], bf16x8& w0, bf16x8& w1) {
+    w0 = operand(p, 0);
+    w1 = operand(p, 1);
+  }
+};
+
 }  // namespace moe

@@ -92,13 +92,15 @@ constexpr int stream_block_waves(int KS) { return KS > 1 ? KS : kStreamWaves; }
 
 // A workgroup holds stream_block_waves(KS)/KS items; wave w works on item
 // w/KS and streams the (w%KS)-th slice of its reduction axis.
-template <bool kGateUp, typename Act, bool kScaleBf16, int NG, int RB, int P, int KS>
+template <bool kGateUp, typename Act, bool kScaleBf16, int F, int NG, int RB, int P, int KS>
 __global__ __launch_bounds__(stream_block_waves(KS) * kWave) void ffn_stream_kernel(
     const Act* __restrict__ X, const int32_t* __restrict__ sorted_slots, int topk,
     const int8_t* __restrict__ W0, const int8_t* __restrict__ W1, const void* __restrict__ S0,
     const void* __restrict__ S1, const int32_t* __restrict__ offsets, int E, int N, int Kd,
     void* __restrict__ out) {
   constexpr int NMAT = kGateUp ? 2 : 1;
+  using WF = WFormat<F>;
+  constexpr int PPS = WF::kPieces;  // 1 KiB blocks per group and step
   constexpr int IPW = stream_block_waves(KS) / KS;  // items per workgroup
   // partial sums of slices 1..KS-1 for one 16-row block (KS > 1: one item)
   __shared__ f32x4 red[KS > 1 ? KS - 1 : 1][NG][NMAT][kWave];
@@ -140,17 +142,22 @@ __global__ __launch_bounds__(stream_block_waves(KS) * kWave) void ffn_stream_ker
 #pragma unroll
   for (int ng = 0; ng < NG; ++ng) {
     const long group = ((long)e * N + ch_base + ng * 16) >> 4;
-    const long off = group * (long)(Kd >> 6) * 1024 + 16 * lane;
+    const long off = group * (long)(Kd >> 6) * (1024 * PPS) + 16 * lane;
     wp[ng][0] = W0 + off;
     if constexpr (kGateUp) wp[ng][1] = W1 + off;
   }
   // per-lane scales of the 4 channels this lane holds in the result
+  // (unscaled encodings: 1)
   float4 sc[NG][NMAT];
 #pragma unroll
   for (int ng = 0; ng < NG; ++ng) {
     const long ch = (long)e * N + ch_base + ng * 16 + 4 * lg;
-    sc[ng][0] = load_scale4<kScaleBf16>(S0, ch);
-    if constexpr (kGateUp) sc[ng][1] = load_scale4<kScaleBf16>(S1, ch);
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m) sc[ng][m] = make_float4(1.f, 1.f, 1.f, 1.f);
+    if constexpr (WF::kScaled) {
+      sc[ng][0] = load_scale4<kScaleBf16>(S0, ch);
+      if constexpr (kGateUp) sc[ng][1] = load_scale4<kScaleBf16>(S1, ch);
+    }
   }
 
   // this wave's slice of the 64-wide reduction steps
@@ -175,7 +182,7 @@ __global__ __launch_bounds__(stream_block_waves(KS) * kWave) void ffn_stream_ker
           src = (long)(row0 + r) * Kd;
         }
       }
-      ap[rb] = X + src + 16 * lg + (long)s_base * 64;
+      ap[rb] = X + src + WF::kActLane * lg + (long)s_base * 64;
     }
 
     f32x4 acc[RB][NG][NMAT];
@@ -192,34 +199,37 @@ __global__ __launch_bounds__(stream_block_waves(KS) * kWave) void ffn_stream_ker
     constexpr int PA_WANT = RB >= 4 ? MOE_STREAM_PA_WIDE : P;
     constexpr int PA = PA_WANT < P ? PA_WANT : P;
     constexpr int U = ring_unroll(P, PA);
-    uint4 bw[P][NG][NMAT];
+    uint4 bw[P][NG][NMAT][PPS];
     bf16x8 av[PA][RB][2];
 
-    auto load_w = [&](int s, uint4 (&b)[NG][NMAT]) {
+    auto load_w = [&](int s, uint4 (&b)[NG][NMAT][PPS]) {
 #pragma unroll
       for (int ng = 0; ng < NG; ++ng)
 #pragma unroll
-        for (int m = 0; m < NMAT; ++m) b[ng][m] = load_nt16(wp[ng][m] + (long)(s_base + s) * 1024);
+        for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+          for (int q = 0; q < PPS; ++q) b[ng][m][q] = load_nt16(wp[ng][m] + ((long)(s_base + s) * PPS + q) * 1024);
     };
     auto load_a = [&](int s, bf16x8 (&a)[RB][2]) {
       const long off = (long)s * 64;
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
         if (rb < nrb && aok[rb]) {
-          Act16<Act>::load(ap[rb] + off, a[rb][0], a[rb][1]);
+          a[rb][0] = load_act8(ap[rb] + off);
+          a[rb][1] = load_act8(ap[rb] + off + WF::kActSecond);
         } else {
           a[rb][0] = zero_bf16x8();
           a[rb][1] = zero_bf16x8();
         }
       }
     };
-    auto compute_step = [&](const uint4 (&b)[NG][NMAT], const bf16x8 (&a)[RB][2]) {
+    auto compute_step = [&](const uint4 (&b)[NG][NMAT][PPS], const bf16x8 (&a)[RB][2]) {
 #pragma unroll
       for (int ng = 0; ng < NG; ++ng) {
 #pragma unroll
         for (int m = 0; m < NMAT; ++m) {
-          const bf16x8 w_lo = i8x8_to_bf16(b[ng][m].x, b[ng][m].y);
-          const bf16x8 w_hi = i8x8_to_bf16(b[ng][m].z, b[ng][m].w);
+          bf16x8 w_lo, w_hi;
+          WF::operands(b[ng][m], w_lo, w_hi);
 #pragma unroll
           for (int rb = 0; rb < RB; ++rb) {
             if (rb < nrb) {
@@ -299,7 +309,7 @@ __global__ __launch_bounds__(stream_block_waves(KS) * kWave) void ffn_stream_ker
   }
 }
 
-template <bool kGateUp, typename Act, bool kScaleBf16, int RB, int KS>
+template <bool kGateUp, typename Act, bool kScaleBf16, int F, int RB, int KS>
 hipError_t launch_stream_pass_ks(const FfnArgs& a, long items, hipStream_t stream) {
   constexpr int NG = kGateUp ? MOE_STREAM_NG_GU : (RB >= 4 ? MOE_STREAM_NG_DN_WIDE : MOE_STREAM_NG_DN);
   constexpr int P = kGateUp ? MOE_STREAM_P_GU : MOE_STREAM_P_DN;
@@ -308,47 +318,61 @@ hipError_t launch_stream_pass_ks(const FfnArgs& a, long items, hipStream_t strea
   const dim3 grid((unsigned)(KS > 1 ? items : (items + kStreamWaves - 1) / kStreamWaves));
   const dim3 block(stream_block_waves(KS) * kWave);
   if constexpr (kGateUp) {
-    hipLaunchKernelGGL((ffn_stream_kernel<true, Act, kScaleBf16, NG, RB, P, KS>), grid, block, 0, stream,
+    hipLaunchKernelGGL((ffn_stream_kernel<true, Act, kScaleBf16, F, NG, RB, P, KS>), grid, block, 0, stream,
                        static_cast<const Act*>(a.x), a.sorted_slots, a.K, a.w_gate, a.w_up, a.s_gate, a.s_up,
                        a.offsets, a.E, N, Kd, static_cast<void*>(a.h));
   } else {
-    hipLaunchKernelGGL((ffn_stream_kernel<false, __bf16, kScaleBf16, NG, RB, P, KS>), grid, block, 0, stream,
+    hipLaunchKernelGGL((ffn_stream_kernel<false, __bf16, kScaleBf16, F, NG, RB, P, KS>), grid, block, 0, stream,
                        static_cast<const __bf16*>(a.h), a.sorted_slots, a.K, a.w_down, nullptr, a.s_down,
                        nullptr, a.offsets, a.E, N, Kd, static_cast<void*>(a.y_rows));
   }
   return hipGetLastError();
 }
 
-template <bool kGateUp, typename Act, bool kScaleBf16, int RB>
+template <bool kGateUp, typename Act, bool kScaleBf16, int F, int RB>
 hipError_t launch_stream_pass_rb(const FfnArgs& a, hipStream_t stream) {
   constexpr int NG = kGateUp ? MOE_STREAM_NG_GU : (RB >= 4 ? MOE_STREAM_NG_DN_WIDE : MOE_STREAM_NG_DN);
   const int N = kGateUp ? a.f : a.d;
   const long items = (long)a.E * (N / (16 * NG));
   switch (choose_split(items, RB)) {
-    case 1: return launch_stream_pass_ks<kGateUp, Act, kScaleBf16, RB, 1>(a, items, stream);
-    case 2: return launch_stream_pass_ks<kGateUp, Act, kScaleBf16, RB, 2>(a, items, stream);
-    case 4: return launch_stream_pass_ks<kGateUp, Act, kScaleBf16, RB, 4>(a, items, stream);
-    default: return launch_stream_pass_ks<kGateUp, Act, kScaleBf16, RB, 8>(a, items, stream);
+    case 1: return launch_stream_pass_ks<kGateUp, Act, kScaleBf16, F, RB, 1>(a, items, stream);
+    case 2: return launch_stream_pass_ks<kGateUp, Act, kScaleBf16, F, RB, 2>(a, items, stream);
+    case 4: return launch_stream_pass_ks<kGateUp, Act, kScaleBf16, F, RB, 4>(a, items, stream);
+    default: return launch_stream_pass_ks<kGateUp, Act, kScaleBf16, F, RB, 8>(a, items, stream);
   }
 }
 
 // Rows per pass: 16*RB. More than 32 rows per expert on average (a dense MLP
 // layer, or a hot expert at decode) takes the 64-row variant so the weights
 // are streamed once; otherwise the 32-row variant keeps more waves resident.
-template <bool kGateUp, typename Act, bool kScaleBf16>
+template <bool kGateUp, typename Act, bool kScaleBf16, int F>
 hipError_t launch_stream_pass(const FfnArgs& a, hipStream_t stream) {
-  if ((long)a.S > 32L * a.E) return launch_stream_pass_rb<kGateUp, Act, kScaleBf16, 4>(a, stream);
-  return launch_stream_pass_rb<kGateUp, Act, kScaleBf16, MOE_STREAM_RB>(a, stream);
+  if ((long)a.S > 32L * a.E) return launch_stream_pass_rb<kGateUp, Act, kScaleBf16, F, 4>(a, stream);
+  return launch_stream_pass_rb<kGateUp, Act, kScaleBf16, F, MOE_STREAM_RB>(a, stream);
 }
 
+// int8 weights: fp32 or bf16 activations and scales. bf16 and fp8 weights
+// (comparators): bf16 activations; fp8 takes either scale dtype.
 template <bool kGateUp>
 hipError_t dispatch_stream(const FfnArgs& a, hipStream_t stream) {
-  if (a.act_bf16) {
-    return a.scale_bf16 ? launch_stream_pass<kGateUp, __bf16, true>(a, stream)
-                        : launch_stream_pass<kGateUp, __bf16, false>(a, stream);
+  switch (a.wfmt) {
+    case kWInt8:
+      if (a.act_bf16) {
+        return a.scale_bf16 ? launch_stream_pass<kGateUp, __bf16, true, kWInt8>(a, stream)
+                            : launch_stream_pass<kGateUp, __bf16, false, kWInt8>(a, stream);
+      }
+      return a.scale_bf16 ? launch_stream_pass<kGateUp, float, true, kWInt8>(a, stream)
+                          : launch_stream_pass<kGateUp, float, false, kWInt8>(a, stream);
+    case kWBf16:
+      if (!a.act_bf16) return hipErrorInvalidValue;
+      return launch_stream_pass<kGateUp, __bf16, true, kWBf16>(a, stream);
+    case kWFp8:
+      if (!a.act_bf16) return hipErrorInvalidValue;
+      return a.scale_bf16 ? launch_stream_pass<kGateUp, __bf16, true, kWFp8>(a, stream)
+                          : launch_stream_pass<kGateUp, __bf16, false, kWFp8>(a, stream);
+    default:
+      return hipErrorInvalidValue;
   }
-  return a.scale_bf16 ? launch_stream_pass<kGateUp, float, true>(a, stream)
-                      : launch_stream_pass<kGateUp, float, false>(a, stream);
 }
 
 }  // namespace

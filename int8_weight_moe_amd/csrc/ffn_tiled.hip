@@ -334,6 +334,12 @@ constexpr int waitcnt_vm_lgkm0(int vm) { return (vm & 15) | ((vm >> 4) << 14) | 
 #ifndef MOE_DMA_STAGES
 #define MOE_DMA_STAGES 2
 #endif
+// channel tile of the bf16-weight comparator: its weight tile has twice the
+// bytes per channel, so half the channels keep the LDS footprint (and two
+// workgroups per CU) of the int8 tile
+#ifndef MOE_DMA_BN_BF16
+#define MOE_DMA_BN_BF16 128
+#endif
 
 // Waves per SIMD the register allocation must leave room for: with 4-wave
 // workgroups two workgroups share a CU, so one can compute while the other
@@ -342,7 +348,7 @@ constexpr int waitcnt_vm_lgkm0(int vm) { return (vm & 15) | ((vm >> 4) << 14) | 
 #define MOE_DMA_WAVES_PER_EU 2
 #endif
 
-template <bool kGateUp, bool kScaleBf16, int GM, int BM, int BN, int WM, int WN, int STAGES>
+template <bool kGateUp, bool kScaleBf16, int F, int GM, int BM, int BN, int WM, int WN, int STAGES>
 __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(MOE_DMA_WAVES_PER_EU)))
 void ffn_tiled_dma_kernel(
     const __bf16* __restrict__ X, const int32_t* __restrict__ sorted_slots, int topk,
@@ -351,8 +357,10 @@ void ffn_tiled_dma_kernel(
     int m_tiles, int total_blocks, void* __restrict__ out) {
   constexpr int TM = BM / WM, TN = BN / WN, MB = TM / 16, NB = TN / 16;
   static_assert(STAGES == 2 || STAGES == 3, "ring depth");
+  using WF = WFormat<F>;
+  constexpr int PPS = WF::kPieces;           // 1 KiB blocks per 16 channels and step
   constexpr int A_STAGE = BM * 128;          // bytes per step (bf16, 64 wide)
-  constexpr int B_STAGE = BN * 64;           // bytes per step (int8, 64 wide)
+  constexpr int B_STAGE = BN * 64 * PPS;     // bytes per step (weight encoding, 64 wide)
   constexpr int A_INSTR = A_STAGE / 1024 / (WM * WN);  // 1 KiB loads per wave per step
   constexpr int B_INSTR = B_STAGE / 1024 / (WM * WN);
   constexpr int CH_TILE = kGateUp ? BN / 2 : BN;
@@ -418,13 +426,15 @@ void ffn_tiled_dma_kernel(
     const int chunk = (lane & 7) ^ (r & 7);
     a_off[j] = (src_row * (uint32_t)Kd + (uint32_t)(chunk * 8)) * 2u;
   }
-  // weight sources: instruction j of this wave copies 16-channel block B_INSTR*wave + j of
-  // this expert's matrix (uniform base) at byte offset b_off (+1 KiB per step)
+  // weight sources: instruction j of this wave copies LDS block q = B_INSTR*wave + j,
+  // piece q % PPS of 16-channel block q / PPS of this expert's matrix (uniform base),
+  // at byte offset b_off (+PPS KiB per step)
   const int8_t* b_base[B_INSTR];
   uint32_t b_off[B_INSTR];
 #pragma unroll
   for (int j = 0; j < B_INSTR; ++j) {
-    const int blk = B_INSTR * wave + j;
+    const int blk = (B_INSTR * wave + j) / PPS;
+    const int piece = (B_INSTR * wave + j) % PPS;
     const int8_t* base;
     int chl;
     if constexpr (kGateUp) {
@@ -435,8 +445,8 @@ void ffn_tiled_dma_kernel(
       chl = n0 + 16 * blk;
     }
     if (chl >= N) chl = 0;                // past N: re-read channel group 0 (results unused)
-    b_base[j] = base + (long)e * N * Kd;
-    b_off[j] = (uint32_t)(chl >> 4) * (uint32_t)(Kd >> 6) * 1024u + 16u * lane;
+    b_base[j] = base + (long)e * N * Kd * PPS;
+    b_off[j] = (uint32_t)(chl >> 4) * (uint32_t)(Kd >> 6) * (1024u * PPS) + 1024u * piece + 16u * lane;
   }
 
   // LDS buffers are always named directly (never through a pointer variable) so
@@ -447,7 +457,7 @@ void ffn_tiled_dma_kernel(
     _Pragma("unroll") for (int j = 0; j < A_INSTR; ++j)                                             \
       dma16(X, a_off[j] + (uint32_t)(KT) * 128u, lds_addr(AS) + (A_INSTR * wave + j) * 1024);       \
     _Pragma("unroll") for (int j = 0; j < B_INSTR; ++j)                                             \
-      dma16(b_base[j], b_off[j] + (uint32_t)(KT) * 1024u, lds_addr(BS) + (B_INSTR * wave + j) * 1024); \
+      dma16(b_base[j], b_off[j] + (uint32_t)(KT) * (1024u * PPS), lds_addr(BS) + (B_INSTR * wave + j) * 1024); \
   }
 
   // weight block of the wave's channel block j (LDS block index)
@@ -466,22 +476,24 @@ void ffn_tiled_dma_kernel(
 #pragma unroll
     for (int j = 0; j < NB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-// One 64-wide step: lane (li, lg) reads piece 16*lg + li of each weight block
-// (channel li, reduction bytes 16*lg .. +16; 16 lanes read 256 contiguous
-// bytes, free of bank conflicts) and uses its low half in sub-step 0 and its
-// high half in sub-step 1; the matching activation chunks are 2*lg + ks.
+// One 64-wide step: lane (li, lg) reads piece 16*lg + li of each of the
+// PPS blocks of a 16-channel group (channel li; 16 lanes read 256 contiguous
+// bytes, free of bank conflicts) and turns them into the two MFMA operands of
+// the step (sub-steps ks = 0, 1); the matching activation chunk holds the
+// reduction elements the encoding puts there: kActLane*lg + kActSecond*ks.
 #define MOE_DMA_COMPUTE(AS, BS, MBV)                                                                \
   {                                                                                                 \
-    uint4 wq[NB];                                                                                   \
+    uint4 wq[NB][PPS];                                                                              \
     _Pragma("unroll") for (int j = 0; j < NB; ++j)                                                  \
-      wq[j] = *reinterpret_cast<const uint4*>(&BS[b_block(j) * 1024 + 256 * lg + 16 * li]);        \
+      _Pragma("unroll") for (int q = 0; q < PPS; ++q)                                               \
+        wq[j][q] = *reinterpret_cast<const uint4*>(&BS[(b_block(j) * PPS + q) * 1024 + 256 * lg + 16 * li]); \
     _Pragma("unroll") for (int ks = 0; ks < 2; ++ks) {                                              \
       bf16x8 xf[MB];                                                                                \
       bf16x8 wf[NB];                                                                                \
       _Pragma("unroll") for (int i = 0; i < MB; ++i) {                                              \
         if (i < (MBV)) {                                                                            \
           const int row = wm * TM + i * 16 + li;                                                    \
-          const int chunk = (2 * lg + ks) ^ (row & 7);                                              \
+          const int chunk = ((WF::kActLane * lg + WF::kActSecond * ks) >> 3) ^ (row & 7);           \
           xf[i] = *reinterpret_cast<const bf16x8*>(&AS[row * 128 + chunk * 16]);                    \
         }                                                                                           \
       }                                                                                             \
@@ -497,15 +509,14 @@ void ffn_tiled_dma_kernel(
 #endif
 #if MOE_DMA_SCHED == 0
 #define MOE_DMA_MMA(MBV)                                                                            \
-  _Pragma("unroll") for (int j = 0; j < NB; ++j)                                                    \
-    wf[j] = ks == 0 ? i8x8_to_bf16(wq[j].x, wq[j].y) : i8x8_to_bf16(wq[j].z, wq[j].w);             \
+  _Pragma("unroll") for (int j = 0; j < NB; ++j) wf[j] = WF::operand(wq[j], ks);                    \
   _Pragma("unroll") for (int i = 0; i < MB; ++i)                                                    \
     if (i < (MBV))                                                                                  \
       _Pragma("unroll") for (int j = 0; j < NB; ++j) acc[i][j] = mfma_bf16(wf[j], xf[i], acc[i][j]);
 #else
 #define MOE_DMA_MMA(MBV)                                                                            \
   _Pragma("unroll") for (int j = 0; j < NB; ++j) {                                                  \
-    wf[j] = ks == 0 ? i8x8_to_bf16(wq[j].x, wq[j].y) : i8x8_to_bf16(wq[j].z, wq[j].w);             \
+    wf[j] = WF::operand(wq[j], ks);                                                                 \
     _Pragma("unroll") for (int i = 0; i < MB; ++i)                                                  \
       if (i < (MBV)) acc[i][j] = mfma_bf16(wf[j], xf[i], acc[i][j]);                                \
     if (MOE_DMA_SCHED == 2) {                                                                       \
@@ -578,8 +589,11 @@ void ffn_tiled_dma_kernel(
       for (int j = 0; j < HALF; ++j) {
         const int ch = n0 + wn * (HALF * 16) + j * 16 + 4 * lg;
         if (ch >= N) continue;
-        const float4 sg = load_scale4<kScaleBf16>(S0, (long)e * N + ch);
-        const float4 su = load_scale4<kScaleBf16>(S1, (long)e * N + ch);
+        float4 sg = make_float4(1.f, 1.f, 1.f, 1.f), su = sg;
+        if constexpr (WF::kScaled) {
+          sg = load_scale4<kScaleBf16>(S0, (long)e * N + ch);
+          su = load_scale4<kScaleBf16>(S1, (long)e * N + ch);
+        }
         const float sgv[4] = {sg.x, sg.y, sg.z, sg.w}, suv[4] = {su.x, su.y, su.z, su.w};
         bf16x4 hv;
 #pragma unroll
@@ -591,12 +605,38 @@ void ffn_tiled_dma_kernel(
       for (int j = 0; j < NB; ++j) {
         const int ch = n0 + wn * TN + j * 16 + 4 * lg;
         if (ch >= N) continue;
-        const float4 sd = load_scale4<kScaleBf16>(S0, (long)e * N + ch);
+        float4 sd = make_float4(1.f, 1.f, 1.f, 1.f);
+        if constexpr (WF::kScaled) sd = load_scale4<kScaleBf16>(S0, (long)e * N + ch);
         const float4 yv = make_float4(acc[i][j][0] * sd.x, acc[i][j][1] * sd.y, acc[i][j][2] * sd.z, acc[i][j][3] * sd.w);
         *reinterpret_cast<float4*>(static_cast<float*>(out) + orow + ch) = yv;
       }
     }
   }
+}
+
+template <bool kGateUp, bool kScaleBf16, int F, int DBN>
+hipError_t launch_dma_pass(const FfnArgs& a, hipStream_t stream) {
+  constexpr int GM = MOE_TILE_GM;
+  constexpr int DBM = MOE_DMA_BM, DWM = MOE_DMA_WM, DWN = MOE_DMA_WN, DST = MOE_DMA_STAGES;
+  constexpr int DCH = kGateUp ? DBN / 2 : DBN;
+  const int N = kGateUp ? a.f : a.d;
+  const int Kd = kGateUp ? a.d : a.f;
+  const int dn_tiles = (N + DCH - 1) / DCH;
+  const long dm_tiles = (long)(a.S + DBM - 1) / DBM + a.E;
+  const long dblocks = (dm_tiles * dn_tiles + kXcds - 1) / kXcds * kXcds;
+  const dim3 dblock(DWM * DWN * kWave);
+  if constexpr (kGateUp) {
+    hipLaunchKernelGGL((ffn_tiled_dma_kernel<true, kScaleBf16, F, GM, DBM, DBN, DWM, DWN, DST>), dim3((unsigned)dblocks),
+                       dblock, 0, stream, static_cast<const __bf16*>(a.x), a.sorted_slots, a.K, a.w_gate, a.w_up,
+                       a.s_gate, a.s_up, a.offsets, a.E, N, Kd, dn_tiles, (int)dm_tiles, (int)dblocks,
+                       static_cast<void*>(a.h));
+  } else {
+    hipLaunchKernelGGL((ffn_tiled_dma_kernel<false, kScaleBf16, F, GM, DBM, DBN, DWM, DWN, DST>), dim3((unsigned)dblocks),
+                       dblock, 0, stream, static_cast<const __bf16*>(a.h), a.sorted_slots, a.K, a.w_down, nullptr,
+                       a.s_down, nullptr, a.offsets, a.E, N, Kd, dn_tiles, (int)dm_tiles, (int)dblocks,
+                       static_cast<void*>(a.y_rows));
+  }
+  return hipGetLastError();
 }
 
 template <bool kGateUp, typename Act, bool kScaleBf16>
@@ -605,6 +645,9 @@ hipError_t launch_tiled_pass(const FfnArgs& a, hipStream_t stream) {
   constexpr int CH_TILE = kGateUp ? BN / 2 : BN;
   const int N = kGateUp ? a.f : a.d;
   const int Kd = kGateUp ? a.d : a.f;
+  if (sizeof(Act) == 2 && MOE_TILE_DMA && dma_offsets_fit(a.T, a.S, a.d, a.f, 1))
+    return launch_dma_pass<kGateUp, kScaleBf16, kWInt8, MOE_DMA_BN>(a, stream);
+  // register-staged kernel (int8 weights only)
   const int n_tiles_n = (N + CH_TILE - 1) / CH_TILE;
   // row tiles: at most one partial tile per expert beyond S / BM
   const long m_tiles_max = (long)(a.S + BM - 1) / BM + a.E;
@@ -612,30 +655,6 @@ hipError_t launch_tiled_pass(const FfnArgs& a, hipStream_t stream) {
   blocks = (blocks + kXcds - 1) / kXcds * kXcds;
   const dim3 grid((unsigned)blocks);
   const dim3 block(WM * WN * kWave);
-  // the direct-to-LDS kernel addresses with 32-bit byte offsets from the
-  // activation tensor and from one expert's weight matrix
-  const uint64_t act_bytes = kGateUp ? (uint64_t)a.T * a.d * 2 : (uint64_t)a.S * a.f * 2;
-  const bool offsets_fit = act_bytes < (1ull << 32) && (uint64_t)N * Kd < (1ull << 32);
-  if (sizeof(Act) == 2 && MOE_TILE_DMA && offsets_fit) {
-    constexpr int DBM = MOE_DMA_BM, DBN = MOE_DMA_BN, DWM = MOE_DMA_WM, DWN = MOE_DMA_WN, DST = MOE_DMA_STAGES;
-    constexpr int DCH = kGateUp ? DBN / 2 : DBN;
-    const int dn_tiles = (N + DCH - 1) / DCH;
-    const long dm_tiles = (long)(a.S + DBM - 1) / DBM + a.E;
-    long dblocks = (dm_tiles * dn_tiles + kXcds - 1) / kXcds * kXcds;
-    const dim3 dblock(DWM * DWN * kWave);
-    if constexpr (kGateUp) {
-      hipLaunchKernelGGL((ffn_tiled_dma_kernel<true, kScaleBf16, GM, DBM, DBN, DWM, DWN, DST>), dim3((unsigned)dblocks),
-                         dblock, 0, stream, static_cast<const __bf16*>(a.x), a.sorted_slots, a.K, a.w_gate, a.w_up,
-                         a.s_gate, a.s_up, a.offsets, a.E, N, Kd, dn_tiles, (int)dm_tiles, (int)dblocks,
-                         static_cast<void*>(a.h));
-    } else {
-      hipLaunchKernelGGL((ffn_tiled_dma_kernel<false, kScaleBf16, GM, DBM, DBN, DWM, DWN, DST>), dim3((unsigned)dblocks),
-                         dblock, 0, stream, static_cast<const __bf16*>(a.h), a.sorted_slots, a.K, a.w_down, nullptr,
-                         a.s_down, nullptr, a.offsets, a.E, N, Kd, dn_tiles, (int)dm_tiles, (int)dblocks,
-                         static_cast<void*>(a.y_rows));
-    }
-    return hipGetLastError();
-  }
   if constexpr (kGateUp) {
     hipLaunchKernelGGL((ffn_tiled_kernel<true, Act, kScaleBf16, BM, BN, WM, WN, GM>), grid, block, 0, stream,
                        static_cast<const Act*>(a.x), a.sorted_slots, a.K, a.w_gate, a.w_up, a.s_gate, a.s_up,
@@ -648,17 +667,40 @@ hipError_t launch_tiled_pass(const FfnArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// int8 weights: every activation and scale dtype (the register-staged kernel
+// covers fp32 activations and tensors past 32-bit offsets). bf16 and fp8
+// weights (comparators): the direct-to-LDS kernel only, bf16 activations.
 template <bool kGateUp>
 hipError_t dispatch_tiled(const FfnArgs& a, hipStream_t stream) {
-  if (a.act_bf16) {
-    return a.scale_bf16 ? launch_tiled_pass<kGateUp, __bf16, true>(a, stream)
-                        : launch_tiled_pass<kGateUp, __bf16, false>(a, stream);
+  switch (a.wfmt) {
+    case kWInt8:
+      if (a.act_bf16) {
+        return a.scale_bf16 ? launch_tiled_pass<kGateUp, __bf16, true>(a, stream)
+                            : launch_tiled_pass<kGateUp, __bf16, false>(a, stream);
+      }
+      return a.scale_bf16 ? launch_tiled_pass<kGateUp, float, true>(a, stream)
+                          : launch_tiled_pass<kGateUp, float, false>(a, stream);
+    case kWBf16:
+      if (!a.act_bf16 || !dma_offsets_fit(a.T, a.S, a.d, a.f, 2)) return hipErrorInvalidValue;
+      return launch_dma_pass<kGateUp, true, kWBf16, MOE_DMA_BN_BF16>(a, stream);
+    case kWFp8:
+      if (!a.act_bf16 || !dma_offsets_fit(a.T, a.S, a.d, a.f, 1)) return hipErrorInvalidValue;
+      return a.scale_bf16 ? launch_dma_pass<kGateUp, true, kWFp8, MOE_DMA_BN>(a, stream)
+                          : launch_dma_pass<kGateUp, false, kWFp8, MOE_DMA_BN>(a, stream);
+    default:
+      return hipErrorInvalidValue;
   }
-  return a.scale_bf16 ? launch_tiled_pass<kGateUp, float, true>(a, stream)
-                      : launch_tiled_pass<kGateUp, float, false>(a, stream);
 }
 
 }  // namespace
+
+// The direct-to-LDS kernel addresses with 32-bit byte offsets from the
+// activation tensors (x [T, d], h [S, f] bf16) and from one expert's weight
+// matrix (f*d elements of wbytes each).
+bool dma_offsets_fit(long T, long S, long d, long f, int wbytes) {
+  const uint64_t lim = 1ull << 32;
+  return (uint64_t)T * d * 2 < lim && (uint64_t)S * f * 2 < lim && (uint64_t)d * f * wbytes < lim;
+}
 
 hipError_t launch_tiled_gate_up(const FfnArgs& a, hipStream_t stream) { return dispatch_tiled<true>(a, stream); }
 hipError_t launch_tiled_down(const FfnArgs& a, hipStream_t stream) { return dispatch_tiled<false>(a, stream); }

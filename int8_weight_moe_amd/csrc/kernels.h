@@ -21,10 +21,11 @@ struct FfnArgs {
   bool scale_bf16;            // scale dtype
   const int32_t* offsets;     // [E + 1]
   const int32_t* sorted_slots;  // [S]
-  const int8_t* w_gate;       // [E, f, d], tiled int8 layout
-  const int8_t* w_up;         // [E, f, d], tiled int8 layout
-  const int8_t* w_down;       // [E, d, f], tiled int8 layout
-  const void* s_gate;         // [E, f]
+  int wfmt;                   // weight encoding (WFmt: int8, bf16 or fp8)
+  const int8_t* w_gate;       // [E, f, d], tiled layout of the weight bytes
+  const int8_t* w_up;         // [E, f, d], tiled layout of the weight bytes
+  const int8_t* w_down;       // [E, d, f], tiled layout of the weight bytes
+  const void* s_gate;         // [E, f] (unused for bf16 weights)
   const void* s_up;           // [E, f]
   const void* s_down;         // [E, d]
   __bf16* h;                  // [S, f] scratch
@@ -36,7 +37,10 @@ struct FfnArgs {
 // (x -> h) and down pass (h -> y_rows).
 hipError_t launch_stream_gate_up(const FfnArgs& a, hipStream_t stream);
 hipError_t launch_stream_down(const FfnArgs& a, hipStream_t stream);
-// Tiled MFMA schedule for many rows per expert (prefill).
+// Tiled MFMA schedule for many rows per expert (prefill). bf16 and fp8
+// weights need bf16 activations and dma_offsets_fit(T, S, d, f, bytes per
+// weight); int8 weights take any shape.
+bool dma_offsets_fit(long T, long S, long d, long f, int wbytes);
 hipError_t launch_tiled_gate_up(const FfnArgs& a, hipStream_t stream);
 hipError_t launch_tiled_down(const FfnArgs& a, hipStream_t stream);
 

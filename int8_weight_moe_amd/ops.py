@@ -14,25 +14,30 @@ from typing import Optional
 import torch
 
 from . import _lib
-from ._lib import MOE_BF16, MOE_F32, MOE_PATH_AUTO, MOE_PATH_STREAM, MOE_PATH_TILED, MoeError, MoeShape  # noqa: F401
+from ._lib import (MOE_BF16, MOE_F32, MOE_PATH_AUTO, MOE_PATH_STREAM, MOE_PATH_TILED, MOE_W_BF16,  # noqa: F401
+                   MOE_W_FP8, MOE_W_INT8, MoeError, MoeShape)
 
 _DT = {torch.float32: MOE_F32, torch.bfloat16: MOE_BF16}
 
 
 @dataclasses.dataclass
 class Int8Experts:
-    """ExpertsInt8 weights of one MoE layer: int8 codes plus per-output-channel scales.
+    """Expert weights of one MoE layer as the FFN kernels read them.
 
-    q_gate, q_up [E, f, d] int8; q_down [E, d, f] int8, each holding its codes in
-    the tiled layout of moe_pack_rows (the tensor shape is kept for the sizes);
-    s_gate, s_up [E, f]; s_down [E, d] (scales all fp32 or all bf16).
+    fmt MOE_W_INT8 (ExpertsInt8, the default): q_gate, q_up [E, f, d] int8 and
+    q_down [E, d, f] int8 codes plus per-output-channel scales s_gate, s_up
+    [E, f], s_down [E, d] (all fp32 or all bf16). fmt MOE_W_FP8: the same with
+    OCP e4m3 codes (uint8 tensors). fmt MOE_W_BF16 (comparator): q_* are the
+    bf16 weights themselves and s_* are None. Every q_* holds its bytes in the
+    tiled layout of moe_pack_rows; the tensor shape is kept for the sizes.
     """
     q_gate: torch.Tensor
     q_up: torch.Tensor
     q_down: torch.Tensor
-    s_gate: torch.Tensor
-    s_up: torch.Tensor
-    s_down: torch.Tensor
+    s_gate: Optional[torch.Tensor]
+    s_up: Optional[torch.Tensor]
+    s_down: Optional[torch.Tensor]
+    fmt: int = MOE_W_INT8
 
     @property
     def E(self) -> int:
@@ -48,7 +53,7 @@ class Int8Experts:
 
     @property
     def scale_dtype(self) -> torch.dtype:
-        return self.s_gate.dtype
+        return self.s_gate.dtype if self.s_gate is not None else torch.bfloat16
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -70,8 +75,8 @@ def _dtype_code(dt: torch.dtype) -> int:
 
 
 def make_shape(T: int, d: int, f: int, E: int, K: int, act: torch.dtype, scale: torch.dtype,
-               path: int = MOE_PATH_AUTO) -> MoeShape:
-    return MoeShape(T, d, f, E, K, _dtype_code(act), _dtype_code(scale), path)
+               path: int = MOE_PATH_AUTO, fmt: int = MOE_W_INT8) -> MoeShape:
+    return MoeShape(T, d, f, E, K, _dtype_code(act), _dtype_code(scale), path, fmt)
 
 
 def _lib_handle():
@@ -125,7 +130,7 @@ def moe_expert_ffn(x: torch.Tensor, expert_offsets: torch.Tensor, sorted_slots: 
     """Expert SwiGLU FFNs on the permuted rows. Returns y_rows fp32 [T*K, d] (sorted-row order)."""
     lib = _lib_handle()
     T, d = x.shape
-    shape = make_shape(T, d, experts.f, experts.E, K, x.dtype, experts.scale_dtype, path)
+    shape = make_shape(T, d, experts.f, experts.E, K, x.dtype, experts.scale_dtype, path, experts.fmt)
     y_rows = torch.empty((T * K, d), dtype=torch.float32, device=x.device)
     need = ffn_workspace_size(shape)
     if workspace is None:
@@ -143,7 +148,7 @@ def moe_expert_gate_up(x: torch.Tensor, expert_offsets: torch.Tensor, sorted_slo
     """Gate/up pass: h [T*K, f] bf16 (sorted-row order)."""
     lib = _lib_handle()
     T, d = x.shape
-    shape = make_shape(T, d, experts.f, experts.E, K, x.dtype, experts.scale_dtype, path)
+    shape = make_shape(T, d, experts.f, experts.E, K, x.dtype, experts.scale_dtype, path, experts.fmt)
     if h is None:
         h = torch.empty((T * K, experts.f), dtype=torch.bfloat16, device=x.device)
     _lib.check(lib.moe_expert_gate_up(
@@ -157,7 +162,7 @@ def moe_expert_down(h: torch.Tensor, expert_offsets: torch.Tensor, experts: Int8
                     y_rows: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Down pass: y_rows [T*K, d] fp32 from h [T*K, f] bf16."""
     lib = _lib_handle()
-    shape = make_shape(T, experts.d, experts.f, experts.E, K, act, experts.scale_dtype, path)
+    shape = make_shape(T, experts.d, experts.f, experts.E, K, act, experts.scale_dtype, path, experts.fmt)
     if y_rows is None:
         y_rows = torch.empty((T * K, experts.d), dtype=torch.float32, device=h.device)
     _lib.check(lib.moe_expert_down(ctypes.byref(shape), _ptr(h), _ptr(expert_offsets), _ptr(experts.q_down),
@@ -201,7 +206,7 @@ class MoeLayer:
 
     def shape(self, x: torch.Tensor, path: int = MOE_PATH_AUTO) -> MoeShape:
         e = self.experts
-        return make_shape(x.shape[0], x.shape[1], e.f, e.E, self.K, x.dtype, e.scale_dtype, path)
+        return make_shape(x.shape[0], x.shape[1], e.f, e.E, self.K, x.dtype, e.scale_dtype, path, e.fmt)
 
 
 def moe_forward(x: torch.Tensor, router_w: torch.Tensor, bias: Optional[torch.Tensor], experts: Int8Experts,
@@ -211,7 +216,7 @@ def moe_forward(x: torch.Tensor, router_w: torch.Tensor, bias: Optional[torch.Te
     """The whole layer. Returns (y [T, d] in x.dtype, topk_ids [T, K], topk_w [T, K])."""
     lib = _lib_handle()
     T, d = x.shape
-    shape = make_shape(T, d, experts.f, experts.E, K, x.dtype, experts.scale_dtype, path)
+    shape = make_shape(T, d, experts.f, experts.E, K, x.dtype, experts.scale_dtype, path, experts.fmt)
     dev = x.device
     if y is None:
         y = torch.empty((T, d), dtype=x.dtype, device=dev)
@@ -235,7 +240,7 @@ def moe_mlp_forward(x: torch.Tensor, experts: Int8Experts, path: int = MOE_PATH_
     T, d = x.shape
     if experts.E != 1:
         raise ValueError("the dense MLP takes one expert (E = 1)")
-    shape = make_shape(T, d, experts.f, 1, 1, x.dtype, experts.scale_dtype, path)
+    shape = make_shape(T, d, experts.f, 1, 1, x.dtype, experts.scale_dtype, path, experts.fmt)
     if y is None:
         y = torch.empty((T, d), dtype=x.dtype, device=x.device)
     if workspace is None:
@@ -269,6 +274,17 @@ def moe_pack_rows(q: torch.Tensor) -> torch.Tensor:
     out = torch.empty_like(q)
     _lib.check(lib.moe_pack_rows(ctypes.c_int64(rows), ctypes.c_int32(cols), _ptr(q), _ptr(out), _stream()))
     return out
+
+
+def pack_bf16_experts(w_gate: torch.Tensor, w_up: torch.Tensor, w_down: torch.Tensor) -> Int8Experts:
+    """bf16 expert weights (the unquantized comparator) -> the tiled layout of their bytes."""
+    out = []
+    for w in (w_gate, w_up, w_down):
+        if w.dtype != torch.bfloat16:
+            raise TypeError("pack_bf16_experts takes bf16 weights")
+        b = w.contiguous().view(torch.int8)           # [..., rows, 2*cols] bytes
+        out.append(moe_pack_rows(b).view(torch.bfloat16))
+    return Int8Experts(out[0], out[1], out[2], None, None, None, fmt=MOE_W_BF16)
 
 
 def pack_experts(q_gate: torch.Tensor, q_up: torch.Tensor, q_down: torch.Tensor, s_gate: torch.Tensor,

@@ -41,9 +41,11 @@ def test_header_constants_match_binding():
     for name, val in (("MOE_OK", 0), ("MOE_ERR_NULL", 1), ("MOE_ERR_SHAPE", 2), ("MOE_ERR_DTYPE", 3),
                       ("MOE_ERR_ALIGN", 4), ("MOE_ERR_WORKSPACE", 5), ("MOE_ERR_UNSUPPORTED", 6),
                       ("MOE_ERR_HIP", 7), ("MOE_F32", 0), ("MOE_BF16", 1), ("MOE_PATH_AUTO", 0),
-                      ("MOE_PATH_STREAM", 1), ("MOE_PATH_TILED", 2)):
+                      ("MOE_PATH_STREAM", 1), ("MOE_PATH_TILED", 2), ("MOE_W_INT8", 0), ("MOE_W_BF16", 1),
+                      ("MOE_W_FP8", 2)):
         assert re.search(rf"\b{name}\s*=\s*{val}\b", text), name
-    assert ctypes.sizeof(_lib.MoeShape) == 32
+    assert ctypes.sizeof(_lib.MoeShape) == 36
+    assert re.search(r"#define MOE_ABI_VERSION\s+%d\b" % _lib.ABI_VERSION, text)
 
 
 def test_status_strings(lib):
@@ -67,7 +69,7 @@ MIS = ctypes.c_void_p(0x10008)
 @pytest.mark.parametrize("kw,status", [
     (dict(T=-1), 2), (dict(d=100), 2), (dict(d=0), 2), (dict(f=96), 2), (dict(E=0), 2), (dict(E=65), 2),
     (dict(K=0), 2), (dict(K=17), 2), (dict(E=4, K=5), 2), (dict(K=9, E=16), 2), (dict(act_dtype=5), 3),
-    (dict(scale_dtype=-1), 3), (dict(ffn_path=3), 2),
+    (dict(scale_dtype=-1), 3), (dict(ffn_path=3), 2), (dict(weight_fmt=3), 3), (dict(weight_fmt=-1), 3),
 ])
 def test_shape_validation(lib, kw, status):
     n = ctypes.c_size_t(0)
@@ -147,3 +149,24 @@ def test_quantize_validation(lib):
     assert lib.moe_quantize_rows(4, 64, 1, A, 1, None, A, None) == 1
     assert lib.moe_quantize_rows(4, 64, 1, MIS, 1, A, A, None) == 4
     assert lib.moe_quantize_rows(0, 64, 1, A, 1, A, A, None) == 0
+
+
+def test_weight_format_rules(lib):
+    # bf16 weights carry no scales: NULL scale pointers pass validation
+    s = _shape(T=0, weight_fmt=1)
+    n = ctypes.c_size_t(0)
+    assert lib.moe_workspace_size(ctypes.byref(s), ctypes.byref(n)) == 0
+    assert lib.moe_forward(ctypes.byref(s), A, A, None, A, A, A, None, None, None, A, None, None, A,
+                           ctypes.c_size_t(n.value), None) == 0
+    # int8 and fp8 weights need their scales
+    for fmt in (0, 2):
+        s = _shape(T=0, weight_fmt=fmt)
+        assert lib.moe_forward(ctypes.byref(s), A, A, None, A, A, A, None, A, A, A, None, None, A,
+                               ctypes.c_size_t(1 << 30), None) == 1
+    # the comparator encodings run with bf16 activations only
+    for fmt in (1, 2):
+        s = _shape(T=8, act_dtype=0, weight_fmt=fmt)
+        assert lib.moe_forward(ctypes.byref(s), A, A, None, A, A, A, A, A, A, A, None, None, A,
+                               ctypes.c_size_t(1 << 30), None) == 6
+        assert b"bf16 activations" in lib.moe_last_error()
+        assert lib.moe_expert_down(ctypes.byref(s), A, A, A, A, A, None) == 6
