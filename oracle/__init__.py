@@ -12,7 +12,11 @@ calls it, and it imports nothing from the product path.
 
 Modules:
   quant -- per-output-channel symmetric int8 quantizer and bf16 rounding.
-  moe   -- router, top-K gate, permutation, SwiGLU experts, combine.
+  fp8   -- OCP e4m3 encoding and the per-output-channel fp8 quantizer of the
+           FP8 weight comparator (the paper compares ExpertsInt8 with FP8).
+  moe   -- router, top-K gate, permutation, SwiGLU experts, combine (the
+           expert FFN takes any codes and per-row scales: int8, e4m3 values,
+           or bf16 weights with unit scales).
 
 Readings taken where the paper is silent:
   * gate = softmax over all n logits, keep the K largest, renormalise;
@@ -25,4 +29,4 @@ Readings taken where the paper is silent:
 Every function's parity is pinned by tests that do not reuse its own formula:
 see tests/test_oracle_*.py.
 """
-from . import quant, moe  # noqa: F401
+from . import quant, fp8, moe  # noqa: F401

@@ -8,7 +8,8 @@ not be pinning anything.
 import numpy as np
 import pytest
 
-from oracle import moe, quant
+from oracle import fp8, moe, quant
+import tests.test_oracle_fp8 as pf
 import tests.test_oracle_moe as pm
 import tests.test_oracle_quant as pq
 
@@ -108,6 +109,43 @@ def _permute_unstable(ids, E):
     return off, ss, s2r
 
 
+def _e4m3_truncate(v):
+    v = np.asarray(v, dtype=np.float64)
+    _, e = np.frexp(v)
+    step = np.maximum(e - 4, -9)
+    return np.clip(np.ldexp(np.trunc(np.ldexp(v, -step)), step), -448.0, 448.0)
+
+
+def _e4m3_no_saturation(v):
+    v = np.asarray(v, dtype=np.float64)
+    _, e = np.frexp(v)
+    step = np.maximum(e - 4, -9)
+    return np.ldexp(np.rint(np.ldexp(v, -step)), step)
+
+
+def _e4m3_fnuz_range(v):
+    v = np.asarray(v, dtype=np.float64)
+    _, e = np.frexp(v)
+    step = np.maximum(e - 4, -10)
+    return np.clip(np.ldexp(np.rint(np.ldexp(v, -step)), step), -240.0, 240.0)
+
+
+def _e4m3_decode_bias8(codes):
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    ef, mf = (c >> 3) & 0xF, c & 0x7
+    val = sign * np.where(ef == 0, np.ldexp(mf.astype(np.float64), -10), np.ldexp(1.0 + mf / 8.0, ef - 8))
+    return np.where((c & 0x7F) == 0x7F, np.nan, val)
+
+
+def _fp8_scale_240(w, scale_dtype):
+    w = np.asarray(w, dtype=np.float64)
+    s = quant.round_to(np.max(np.abs(w), axis=-1) / 240.0, scale_dtype)
+    safe = np.where(s > 0, s, 1.0)
+    q = fp8.round_to_e4m3(w / safe[..., None])
+    return fp8.e4m3_encode(np.where((s > 0)[..., None], q, 0.0)), s
+
+
 MUTATIONS = [
     ("moe", "expert_swiglu", _swiglu_no_up_scale, [pm.test_single_expert_is_textbook_swiglu_mlp]),
     ("moe", "expert_swiglu", _swiglu_swapped, [pm.test_single_expert_is_textbook_swiglu_mlp]),
@@ -121,12 +159,17 @@ MUTATIONS = [
     ("quant", "quantize_rows", _quant_half_away, [pq.test_quantize_ties_go_to_even]),
     ("quant", "round_to_bf16", _bf16_seven_bits, [pq.test_round_to_bf16_matches_torch_conversion]),
     ("quant", "round_to_bf16", _bf16_truncate, [pq.test_round_to_bf16_matches_torch_conversion]),
+    ("fp8", "round_to_e4m3", _e4m3_truncate, [pf.test_round_matches_torch_conversion]),
+    ("fp8", "round_to_e4m3", _e4m3_no_saturation, [pf.test_round_saturates_and_ties_to_even]),
+    ("fp8", "round_to_e4m3", _e4m3_fnuz_range, [pf.test_round_matches_brute_force_nearest]),
+    ("fp8", "e4m3_decode", _e4m3_decode_bias8, [pf.test_decode_matches_torch_for_every_code]),
+    ("fp8", "quantize_rows_fp8", _fp8_scale_240, [pf.test_quantize_fp8_absmax_lands_on_448_and_round_trip_bound]),
 ]
 
 
 @pytest.mark.parametrize("mod,name,bad,pins", MUTATIONS, ids=[f"{m[1]}:{m[2].__name__}" for m in MUTATIONS])
 def test_pins_catch_planted_mistake(monkeypatch, mod, name, bad, pins):
-    target = moe if mod == "moe" else quant
+    target = {"moe": moe, "quant": quant, "fp8": fp8}[mod]
     monkeypatch.setitem(moe.__dict__, "_orig_permute", moe.permute)
     monkeypatch.setattr(target, name, bad)
     if mod == "quant" and name == "round_to_bf16":
