@@ -48,7 +48,7 @@ def parse():
     ap.add_argument("--no-prefill", action="store_true", help="skip the sibling prefill workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-compare", action="store_true",
-                    help="skip the weight-encoding comparators (the same layer with bf16 weights)")
+                    help="skip the weight-encoding comparators (the same layer with bf16 or fp8 weights)")
     ap.add_argument("--cpu-sample-experts", type=int, default=4)
     ap.add_argument("--path", choices=["auto", "stream", "tiled"], default="auto")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -90,8 +90,8 @@ def touched_rows(layer, x, path):
 def algorithmic(w, counts, wfmt="int8"):
     """Bytes and flops the layer (and each contraction kernel) must move / compute.
 
-    wfmt: weight encoding -- int8 (1 byte per weight plus per-channel scales) or
-    bf16 (2 bytes per weight, no scales)."""
+    wfmt: weight encoding -- int8 or fp8 (1 byte per weight plus per-channel
+    scales) or bf16 (2 bytes per weight, no scales)."""
     ab = 4 if w.act == "f32" else 2
     wb = 2 if wfmt == "bf16" else 1
     sb = 0 if wfmt == "bf16" else (4 if w.scale == "f32" else 2)
@@ -385,17 +385,21 @@ def main():
 
     # weight-encoding comparators: the same layer, inputs and schedule choice
     if not args.no_compare and w.act == "bf16" and w.weight_src == "bf16":
-        from int8_weight_moe_amd import MoeLayer, pack_bf16_experts
+        from int8_weight_moe_amd import MoeLayer, pack_bf16_experts, quantize_experts_fp8
         comp = {}
-        for name in ("bf16",):
-            ex = pack_bf16_experts(src["w_gate"], src["w_up"], src["w_down"])
+        for name in ("bf16", "fp8"):
+            if name == "bf16":
+                ex = pack_bf16_experts(src["w_gate"], src["w_up"], src["w_down"])
+            else:
+                ex = quantize_experts_fp8(src["w_gate"], src["w_up"], src["w_down"], workloads.TORCH_DTYPE[w.scale])
             clayer = MoeLayer(layer.router_w, layer.bias, ex, w.K)
             cms, _ = time_forward(clayer, x, path, args.steps, args.warmup, dense)
             cst = time_stages(clayer, x, path, args.steps, args.warmup, dense)
             calg = algorithmic(w, counts, wfmt=name)
             log(f"{name} weights: {cms * 1e3:.1f} us/step; stages (us): "
                 + ", ".join(f"{k}={v:.1f}" for k, v in cst.items()))
-            entry = {"weights": "bf16 as stored, no scales" if name == "bf16" else name,
+            entry = {"weights": "bf16 as stored, no scales" if name == "bf16" else
+                     f"fp8 e4m3 per-output-channel, {w.scale} scales",
                      "ms_per_step": round(cms, 4), "tokens_per_s": round(w.T / (cms * 1e-3), 1),
                      "int8_speedup": round(cms / ms, 3),
                      "layer_GB": round(calg["layer_bytes"] / 1e9, 4),

@@ -208,6 +208,19 @@ moe_status moe_mlp_forward(const moe_shape* shape, const void* x,
 moe_status moe_quantize_rows(int64_t rows, int32_t cols, int32_t src_dtype, const void* w,
                              int32_t scale_dtype, int8_t* q, void* s, hipStream_t stream);
 
+/* FP8 comparator quantizer: as moe_quantize_rows with OCP e4m3 codes (the
+ * paper compares ExpertsInt8 with FP8 weights, "Serving Considerations and
+ * Improvements"). Row-wise symmetric, one scale per output channel:
+ *   s[r] = max_i |w[r, i]| / 448 rounded once (nearest-even) to scale_dtype,
+ *   q[r, i] = byte of the e4m3 value nearest to w[r, i] / s[r] (ties to the
+ *   even mantissa), saturated to +-448; a zero value is byte 0x00;
+ *   an all-zero row gives s = 0 and q = 0.
+ * e4m3: sign, 4 exponent bits (bias 7), 3 mantissa bits, subnormals m*2^-9,
+ * largest finite 448, bytes 0x7F/0xFF NaN (never produced).
+ * Same sizes, dtypes and errors as moe_quantize_rows. Bit-exact. */
+moe_status moe_quantize_rows_fp8(int64_t rows, int32_t cols, int32_t src_dtype, const void* w,
+                                 int32_t scale_dtype, uint8_t* q, void* s, hipStream_t stream);
+
 /* Tiled int8 layout of the expert weights (load time, next to the quantizer).
  * The kernels read a wavefront's MFMA operands as whole 1 KiB blocks: a
  * row-major int8 matrix q [rows, cols] (rows % 16 == 0, cols % 64 == 0) is

@@ -140,6 +140,19 @@ moe_status run_down(const moe_shape* s, const moe::FfnArgs& a, hipStream_t strea
   return MOE_OK;
 }
 
+moe_status check_quantize(int64_t rows, int32_t cols, int32_t src_dtype, const void* w, int32_t scale_dtype,
+                          const void* q, const void* s) {
+  if (rows < 0 || rows > 0x7fffffffL) return fail(MOE_ERR_SHAPE, "rows=%ld must be in [0, 2^31)", (long)rows);
+  if (cols < 16 || cols > (1 << 20) || cols % 16) return fail(MOE_ERR_SHAPE, "cols=%d must be a multiple of 16 in [16, 2^20]", cols);
+  if (src_dtype != MOE_F32 && src_dtype != MOE_BF16) return fail(MOE_ERR_DTYPE, "src_dtype=%d", src_dtype);
+  if (scale_dtype != MOE_F32 && scale_dtype != MOE_BF16) return fail(MOE_ERR_DTYPE, "scale_dtype=%d", scale_dtype);
+  REQUIRE_PTR(w);
+  REQUIRE_PTR(q);
+  if (!s) return fail(MOE_ERR_NULL, "s is NULL");
+  if ((reinterpret_cast<uintptr_t>(s) & 3u) != 0) return fail(MOE_ERR_ALIGN, "s is not 4-byte aligned");
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -393,17 +406,22 @@ moe_status moe_mlp_forward(const moe_shape* s, const void* x, const void* w_gate
 
 moe_status moe_quantize_rows(int64_t rows, int32_t cols, int32_t src_dtype, const void* w, int32_t scale_dtype,
                              int8_t* q, void* s, hipStream_t stream) {
-  if (rows < 0 || rows > 0x7fffffffL) return fail(MOE_ERR_SHAPE, "rows=%ld must be in [0, 2^31)", (long)rows);
-  if (cols < 16 || cols > (1 << 20) || cols % 16) return fail(MOE_ERR_SHAPE, "cols=%d must be a multiple of 16 in [16, 2^20]", cols);
-  if (src_dtype != MOE_F32 && src_dtype != MOE_BF16) return fail(MOE_ERR_DTYPE, "src_dtype=%d", src_dtype);
-  if (scale_dtype != MOE_F32 && scale_dtype != MOE_BF16) return fail(MOE_ERR_DTYPE, "scale_dtype=%d", scale_dtype);
-  REQUIRE_PTR(w);
-  REQUIRE_PTR(q);
-  if (!s) return fail(MOE_ERR_NULL, "s is NULL");
-  if ((reinterpret_cast<uintptr_t>(s) & 3u) != 0) return fail(MOE_ERR_ALIGN, "s is not 4-byte aligned");
+  const moe_status st = check_quantize(rows, cols, src_dtype, w, scale_dtype, q, s);
+  if (st != MOE_OK) return st;
   if (rows == 0) return MOE_OK;
   const hipError_t e = moe::launch_quantize_rows(rows, cols, src_dtype == MOE_BF16, w, scale_dtype == MOE_BF16, q,
-                                                 s, stream);
+                                                 s, false, stream);
+  if (e != hipSuccess) return hip_fail(e, "quantize launch");
+  return MOE_OK;
+}
+
+moe_status moe_quantize_rows_fp8(int64_t rows, int32_t cols, int32_t src_dtype, const void* w, int32_t scale_dtype,
+                                 uint8_t* q, void* s, hipStream_t stream) {
+  const moe_status st = check_quantize(rows, cols, src_dtype, w, scale_dtype, q, s);
+  if (st != MOE_OK) return st;
+  if (rows == 0) return MOE_OK;
+  const hipError_t e = moe::launch_quantize_rows(rows, cols, src_dtype == MOE_BF16, w, scale_dtype == MOE_BF16,
+                                                 reinterpret_cast<int8_t*>(q), s, true, stream);
   if (e != hipSuccess) return hip_fail(e, "quantize launch");
   return MOE_OK;
 }

@@ -52,7 +52,8 @@ hipError_t launch_dense_init(int T, int32_t* offsets, int32_t* sorted_slots, int
 
 hipError_t launch_pack_rows(long rows, int cols, const int8_t* src, int8_t* dst, hipStream_t stream);
 
+// int8 codes (fp8 = false) or OCP e4m3 code bytes (fp8 = true)
 hipError_t launch_quantize_rows(int64_t rows, int cols, bool src_bf16, const void* w, bool scale_bf16, int8_t* q,
-                                void* s, hipStream_t stream);
+                                void* s, bool fp8, hipStream_t stream);
 
 }  // namespace moe

@@ -13,6 +13,12 @@
 // the 45 dropped mantissa bits), with the subnormal bf16 grid (2^-133) handled
 // separately.
 //
+// The FP8 comparator's quantizer is the same with OCP e4m3 codes: s = a / 448
+// rounded once into the scale dtype, code = the e4m3 value nearest to w / s
+// (ties to the even mantissa) saturated to +-448, encoded as its byte; a zero
+// result is the canonical +0 byte. The e4m3 midpoints have at most 5
+// significant bits, so the same exactness argument holds.
+//
 // One workgroup per row: pass 1 reduces max|w| (16-byte loads, wave shuffles,
 // then LDS across waves), pass 2 re-reads the row (mostly from L2) and writes
 // 16 codes per 16-byte store.
@@ -35,6 +41,30 @@ __device__ __forceinline__ double round_f64_to_bf16(double v) {
   b += ((1ull << 44) - 1ull) + lsb;
   b &= ~((1ull << 45) - 1ull);
   return __longlong_as_double(b);
+}
+
+// byte of the e4m3 value nearest to r (ties to even), saturated to +-448.
+// With a = |r| = m * 2^e (0.5 <= m < 1) the quantum of a's binade is 2^(e-4),
+// never below the subnormal quantum 2^-9; a carry into the next binade gives
+// its first value.
+__device__ __forceinline__ uint32_t encode_e4m3(double r) {
+  const double a = fabs(r);
+  int e;
+  (void)frexp(a, &e);
+  const int step = max(e - 4, -9);
+  double q = ldexp(rint(ldexp(a, -step)), step);
+  q = fmin(q, 448.0);
+  if (q == 0.0) return 0u;
+  uint32_t code;
+  if (q < 0x1p-6) {
+    code = (uint32_t)(q * 0x1p9);                   // exponent field 0: q = M * 2^-9
+  } else {
+    int eq;
+    (void)frexp(q, &eq);                            // q = (1 + M/8) * 2^(eq-1)
+    const uint32_t M = (uint32_t)((ldexp(q, 1 - eq) - 1.0) * 8.0);
+    code = ((uint32_t)(eq - 1 + 7) << 3) | M;
+  }
+  return r < 0.0 ? (code | 0x80u) : code;
 }
 
 template <bool kSrcBf16>
@@ -61,7 +91,7 @@ __device__ __forceinline__ void load16(const void* w, long idx, float (&v)[16]) 
   }
 }
 
-template <bool kSrcBf16, bool kScaleBf16>
+template <bool kSrcBf16, bool kScaleBf16, bool kFp8>
 __global__ __launch_bounds__(kQuantThreads) void quantize_rows_kernel(const void* __restrict__ w, int cols,
                                                                       int8_t* __restrict__ q, void* __restrict__ s) {
   __shared__ float wmax[kQuantThreads / kWave];
@@ -85,7 +115,7 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_rows_kernel(const void
 #pragma unroll
   for (int i = 1; i < kQuantThreads / kWave; ++i) a = fmaxf(a, wmax[i]);
 
-  const double sd = (double)a / 127.0;
+  const double sd = (double)a / (kFp8 ? 448.0 : 127.0);
   double scale;
   if constexpr (kScaleBf16) {
     scale = round_f64_to_bf16(sd);
@@ -107,9 +137,14 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_rows_kernel(const void
     if (scale > 0.0) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        double r = rint((double)v[i] / scale);
-        r = fmin(fmax(r, -127.0), 127.0);
-        const uint32_t b = (uint32_t)(uint8_t)(int8_t)(int)r;
+        uint32_t b;
+        if constexpr (kFp8) {
+          b = encode_e4m3((double)v[i] / scale);
+        } else {
+          double r = rint((double)v[i] / scale);
+          r = fmin(fmax(r, -127.0), 127.0);
+          b = (uint32_t)(uint8_t)(int8_t)(int)r;
+        }
         packed[i >> 2] |= b << (8 * (i & 3));
       }
     }
@@ -117,26 +152,33 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_rows_kernel(const void
   }
 }
 
-}  // namespace
-
-hipError_t launch_quantize_rows(int64_t rows, int cols, bool src_bf16, const void* w, bool scale_bf16, int8_t* q,
-                                void* s, hipStream_t stream) {
+template <bool kFp8>
+hipError_t launch_quantize(int64_t rows, int cols, bool src_bf16, const void* w, bool scale_bf16, int8_t* q, void* s,
+                           hipStream_t stream) {
   if (rows == 0) return hipSuccess;
   const dim3 block(kQuantThreads);
   // grid.x is limited to 2^31-1; rows beyond that are rejected by the caller
   const dim3 grid((unsigned)rows);
   if (src_bf16) {
     if (scale_bf16)
-      hipLaunchKernelGGL((quantize_rows_kernel<true, true>), grid, block, 0, stream, w, cols, q, s);
+      hipLaunchKernelGGL((quantize_rows_kernel<true, true, kFp8>), grid, block, 0, stream, w, cols, q, s);
     else
-      hipLaunchKernelGGL((quantize_rows_kernel<true, false>), grid, block, 0, stream, w, cols, q, s);
+      hipLaunchKernelGGL((quantize_rows_kernel<true, false, kFp8>), grid, block, 0, stream, w, cols, q, s);
   } else {
     if (scale_bf16)
-      hipLaunchKernelGGL((quantize_rows_kernel<false, true>), grid, block, 0, stream, w, cols, q, s);
+      hipLaunchKernelGGL((quantize_rows_kernel<false, true, kFp8>), grid, block, 0, stream, w, cols, q, s);
     else
-      hipLaunchKernelGGL((quantize_rows_kernel<false, false>), grid, block, 0, stream, w, cols, q, s);
+      hipLaunchKernelGGL((quantize_rows_kernel<false, false, kFp8>), grid, block, 0, stream, w, cols, q, s);
   }
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_quantize_rows(int64_t rows, int cols, bool src_bf16, const void* w, bool scale_bf16, int8_t* q,
+                                void* s, bool fp8, hipStream_t stream) {
+  return fp8 ? launch_quantize<true>(rows, cols, src_bf16, w, scale_bf16, q, s, stream)
+             : launch_quantize<false>(rows, cols, src_bf16, w, scale_bf16, q, s, stream);
 }
 
 }  // namespace moe

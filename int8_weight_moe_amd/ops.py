@@ -266,6 +266,18 @@ def moe_quantize_rows(w: torch.Tensor, scale_dtype: torch.dtype):
     return q, s
 
 
+def moe_quantize_rows_fp8(w: torch.Tensor, scale_dtype: torch.dtype):
+    """FP8 comparator quantizer on the GPU: w [..., cols] -> (e4m3 code bytes uint8 [..., cols], s [...])."""
+    lib = _lib_handle()
+    cols = w.shape[-1]
+    rows = w.numel() // cols
+    q = torch.empty(w.shape, dtype=torch.uint8, device=w.device)
+    s = torch.empty(w.shape[:-1], dtype=scale_dtype, device=w.device)
+    _lib.check(lib.moe_quantize_rows_fp8(ctypes.c_int64(rows), ctypes.c_int32(cols), _dtype_code(w.dtype), _ptr(w),
+                                         _dtype_code(scale_dtype), _ptr(q), _ptr(s), _stream()))
+    return q, s
+
+
 def moe_pack_rows(q: torch.Tensor) -> torch.Tensor:
     """Row-major int8 codes [..., rows, cols] -> the tiled layout (same shape, permuted bytes)."""
     lib = _lib_handle()
@@ -291,6 +303,18 @@ def pack_experts(q_gate: torch.Tensor, q_up: torch.Tensor, q_down: torch.Tensor,
                  s_up: torch.Tensor, s_down: torch.Tensor) -> Int8Experts:
     """Row-major int8 codes + scales -> Int8Experts in the kernels' tiled layout."""
     return Int8Experts(moe_pack_rows(q_gate), moe_pack_rows(q_up), moe_pack_rows(q_down), s_gate, s_up, s_down)
+
+
+def quantize_experts_fp8(w_gate: torch.Tensor, w_up: torch.Tensor, w_down: torch.Tensor,
+                         scale_dtype: torch.dtype) -> Int8Experts:
+    """FP8 comparator: quantize the (out, in) expert weights to e4m3 codes, then tile the bytes."""
+    out, scales = [], []
+    for w in (w_gate, w_up, w_down):
+        q, s = moe_quantize_rows_fp8(w, scale_dtype)
+        out.append(moe_pack_rows(q.view(torch.int8)).view(torch.uint8))
+        scales.append(s)
+        del q
+    return Int8Experts(out[0], out[1], out[2], scales[0], scales[1], scales[2], fmt=MOE_W_FP8)
 
 
 def quantize_experts(w_gate: torch.Tensor, w_up: torch.Tensor, w_down: torch.Tensor,
