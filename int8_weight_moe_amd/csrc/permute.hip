@@ -8,10 +8,10 @@
 // One workgroup of 16 waves. Wave w owns a contiguous range of slots, walked
 // in 64-slot chunks. Pass 1 counts, per chunk and expert, the lanes whose id
 // matches (a ballot and a popcount), accumulated by the lane that owns that
-// expert. The 16 x E counts are scanned in LDS in a fixed order (expert-major,
-// then wave). Pass 2 walks the same chunks again and gives each slot its
-// position: the expert's running base plus the number of matching lanes below
-// it in the ballot. Slots therefore keep ascending order inside an expert, and
+// expert. The 16 x E counts are scanned in a fixed order (expert-major, then
+// wave) by the whole workgroup, one count per thread. Pass 2 walks the same
+// chunks again and gives each slot its position: the expert's running base
+// plus the number of matching lanes below it in the ballot. Slots therefore keep ascending order inside an expert, and
 // the result is bit-exact and independent of scheduling.
 #include "device_common.h"
 #include "kernels.h"
@@ -29,6 +29,7 @@ __global__ __launch_bounds__(kPermWaves * kWave) void permute_kernel(const int32
                                                                      int32_t* __restrict__ slot_to_row) {
   __shared__ int cnt[kPermWaves][kMaxExperts];
   __shared__ int base[kPermWaves][kMaxExperts];
+  __shared__ int wave_total[kPermWaves];
   __shared__ int total_valid;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -51,17 +52,32 @@ __global__ __launch_bounds__(kPermWaves * kWave) void permute_kernel(const int32
   cnt[wave][lane] = my_count;
   __syncthreads();
 
-  if (threadIdx.x == 0) {
-    int run = 0;
-    for (int e = 0; e < E; ++e) {
-      offsets[e] = run;
-      for (int w = 0; w < kPermWaves; ++w) {
-        base[w][e] = run;
-        run += cnt[w][e];
-      }
+  // Exclusive scan of the counts in (expert, wave) order, one value per
+  // thread: thread t holds cnt[t % 16][t / 16]. A shuffle scan inside each
+  // wave, then the wave totals through LDS.
+  {
+    const int t = threadIdx.x;
+    const int se = t >> 4, sw = t & 15;
+    const int v = (se < E) ? cnt[sw][se] : 0;
+    int incl = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int n = __shfl_up(incl, off);
+      if (lane >= off) incl += n;
     }
-    offsets[E] = run;
-    total_valid = run;
+    if (lane == 63) wave_total[wave] = incl;
+    __syncthreads();
+    int woff = 0;
+    for (int j = 0; j < wave; ++j) woff += wave_total[j];
+    const int excl = woff + incl - v;
+    if (se < E) {
+      base[sw][se] = excl;
+      if (sw == 0) offsets[se] = excl;
+    }
+    if (t == kPermWaves * kWave - 1) {   // holds the grand total (values past E are 0)
+      offsets[E] = woff + incl;
+      total_valid = woff + incl;
+    }
   }
   __syncthreads();
 

@@ -22,51 +22,74 @@ constexpr int kRouterWaves = 16;
 constexpr int kRouterTokens = 16;
 constexpr int kMaxExperts = 64;
 
-template <typename Act>
+// Eight consecutive elements of row `row` of a [rows, d] tensor at column kk,
+// as bf16 (the MFMA input; fp32 inputs are rounded) or as fp32.
+__device__ __forceinline__ bf16x8 load8(const __bf16* p) { return as_bf16x8(*reinterpret_cast<const uint4*>(p)); }
+
+// Partial logits of one wave: for the 32-wide chunks c = wave, wave + 16, ...
+// of the hidden dimension, the U chunks of a batch are all loaded before any
+// of them is used, so a decode batch (a few tokens: two workgroups in all)
+// keeps U loads in flight per operand instead of one.
+template <typename Act, int EB>
 __device__ __forceinline__ void router_accumulate(const Act* __restrict__ x, const Act* __restrict__ wr,
                                                   int T, int d, int E, int tok0, int wave, int lane,
                                                   f32x4 (&acc)[4]) {
+  constexpr int U = (sizeof(Act) == 2 ? 8 : 4) / EB > 0 ? (sizeof(Act) == 2 ? 8 : 4) / EB : 1;
   const int i = lane & 15;
   const int g = lane >> 4;
   const int tok = tok0 + i;
   const bool tok_ok = tok < T;
-  const int EB = (E + 15) >> 4;
   const int nchunks = d >> 5;  // 32 reduction elements per chunk
-  for (int c = wave; c < nchunks; c += kRouterWaves) {
-    const int kk = c * 32 + 8 * g;
+  for (int c0 = wave; c0 < nchunks; c0 += kRouterWaves * U) {
     if constexpr (sizeof(Act) == 2) {
-      bf16x8 a = tok_ok ? as_bf16x8(*reinterpret_cast<const uint4*>(x + (long)tok * d + kk)) : zero_bf16x8();
+      bf16x8 a[U], b[U][EB];
 #pragma unroll
-      for (int eb = 0; eb < 4; ++eb) {
-        if (eb < EB) {
+      for (int u = 0; u < U; ++u) {
+        const int c = c0 + u * kRouterWaves;
+        const int kk = c * 32 + 8 * g;
+        const bool ok = c < nchunks;
+        a[u] = (ok && tok_ok) ? load8(x + (long)tok * d + kk) : zero_bf16x8();
+#pragma unroll
+        for (int eb = 0; eb < EB; ++eb) {
           const int e = eb * 16 + i;
-          bf16x8 b = (e < E) ? as_bf16x8(*reinterpret_cast<const uint4*>(wr + (long)e * d + kk)) : zero_bf16x8();
-          acc[eb] = mfma_bf16(a, b, acc[eb]);
+          b[u][eb] = (ok && e < E) ? load8(wr + (long)e * d + kk) : zero_bf16x8();
         }
       }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int eb = 0; eb < EB; ++eb) acc[eb] = mfma_bf16(a[u], b[u][eb], acc[eb]);
     } else {
-      float av[8];
-      {
-        float4 p0 = make_float4(0.f, 0.f, 0.f, 0.f), p1 = p0;
-        if (tok_ok) {
+      float4 a[U][2], b[U][EB][2];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int c = c0 + u * kRouterWaves;
+        const int kk = c * 32 + 8 * g;
+        const bool ok = c < nchunks;
+        a[u][0] = a[u][1] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (ok && tok_ok) {
           const float4* q = reinterpret_cast<const float4*>(x + (long)tok * d + kk);
-          p0 = q[0];
-          p1 = q[1];
+          a[u][0] = q[0];
+          a[u][1] = q[1];
         }
-        av[0] = p0.x; av[1] = p0.y; av[2] = p0.z; av[3] = p0.w;
-        av[4] = p1.x; av[5] = p1.y; av[6] = p1.z; av[7] = p1.w;
+#pragma unroll
+        for (int eb = 0; eb < EB; ++eb) {
+          const int e = eb * 16 + i;
+          b[u][eb][0] = b[u][eb][1] = make_float4(0.f, 0.f, 0.f, 0.f);
+          if (ok && e < E) {
+            const float4* q = reinterpret_cast<const float4*>(wr + (long)e * d + kk);
+            b[u][eb][0] = q[0];
+            b[u][eb][1] = q[1];
+          }
+        }
       }
 #pragma unroll
-      for (int eb = 0; eb < 4; ++eb) {
-        if (eb < EB) {
-          const int e = eb * 16 + i;
-          float4 p0 = make_float4(0.f, 0.f, 0.f, 0.f), p1 = p0;
-          if (e < E) {
-            const float4* q = reinterpret_cast<const float4*>(wr + (long)e * d + kk);
-            p0 = q[0];
-            p1 = q[1];
-          }
-          const float bv[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+      for (int u = 0; u < U; ++u) {
+        const float av[8] = {a[u][0].x, a[u][0].y, a[u][0].z, a[u][0].w, a[u][1].x, a[u][1].y, a[u][1].z, a[u][1].w};
+#pragma unroll
+        for (int eb = 0; eb < EB; ++eb) {
+          const float bv[8] = {b[u][eb][0].x, b[u][eb][0].y, b[u][eb][0].z, b[u][eb][0].w,
+                               b[u][eb][1].x, b[u][eb][1].y, b[u][eb][1].z, b[u][eb][1].w};
 #pragma unroll
           for (int j = 0; j < 8; ++j) acc[eb] = mfma_f32(av[j], bv[j], acc[eb]);
         }
@@ -88,7 +111,7 @@ __device__ __forceinline__ void wave_argmax(float& v, int& idx) {
   }
 }
 
-template <typename Act>
+template <typename Act, int EB>
 __global__ __launch_bounds__(kRouterWaves * kWave) void router_topk_kernel(
     const Act* __restrict__ x, const Act* __restrict__ wr, const float* __restrict__ bias,
     int T, int d, int E, int K, int32_t* __restrict__ topk_ids, float* __restrict__ topk_w) {
@@ -100,10 +123,9 @@ __global__ __launch_bounds__(kRouterWaves * kWave) void router_topk_kernel(
   f32x4 acc[4];
 #pragma unroll
   for (int eb = 0; eb < 4; ++eb) acc[eb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  router_accumulate<Act>(x, wr, T, d, E, tok0, wave, lane, acc);
+  router_accumulate<Act, EB>(x, wr, T, d, E, tok0, wave, lane, acc);
 
   // C[token 4*(l/16)+r][expert 16*eb + l%16]
-  const int EB = (E + 15) >> 4;
 #pragma unroll
   for (int eb = 0; eb < 4; ++eb) {
     if (eb < EB) {
@@ -150,20 +172,36 @@ __global__ __launch_bounds__(kRouterWaves * kWave) void router_topk_kernel(
   }
 }
 
+template <typename Act, int EB>
+void launch_router_eb(const void* x, const void* router_w, const float* bias, int T, int d, int E, int K,
+                      int32_t* topk_ids, float* topk_w, hipStream_t stream) {
+  const dim3 grid((T + kRouterTokens - 1) / kRouterTokens);
+  const dim3 block(kRouterWaves * kWave);
+  hipLaunchKernelGGL((router_topk_kernel<Act, EB>), grid, block, 0, stream, static_cast<const Act*>(x),
+                     static_cast<const Act*>(router_w), bias, T, d, E, K, topk_ids, topk_w);
+}
+
+template <typename Act>
+void launch_router_act(const void* x, const void* router_w, const float* bias, int T, int d, int E, int K,
+                       int32_t* topk_ids, float* topk_w, hipStream_t stream) {
+  if (E <= 16) {
+    launch_router_eb<Act, 1>(x, router_w, bias, T, d, E, K, topk_ids, topk_w, stream);
+  } else if (E <= 32) {
+    launch_router_eb<Act, 2>(x, router_w, bias, T, d, E, K, topk_ids, topk_w, stream);
+  } else {
+    launch_router_eb<Act, 4>(x, router_w, bias, T, d, E, K, topk_ids, topk_w, stream);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_router(const void* x, const void* router_w, const float* bias, int T, int d, int E, int K,
                          bool act_bf16, int32_t* topk_ids, float* topk_w, hipStream_t stream) {
   if (T == 0) return hipSuccess;
-  const dim3 grid((T + kRouterTokens - 1) / kRouterTokens);
-  const dim3 block(kRouterWaves * kWave);
   if (act_bf16) {
-    hipLaunchKernelGGL(router_topk_kernel<__bf16>, grid, block, 0, stream,
-                       static_cast<const __bf16*>(x), static_cast<const __bf16*>(router_w), bias, T, d, E, K,
-                       topk_ids, topk_w);
+    launch_router_act<__bf16>(x, router_w, bias, T, d, E, K, topk_ids, topk_w, stream);
   } else {
-    hipLaunchKernelGGL(router_topk_kernel<float>, grid, block, 0, stream, static_cast<const float*>(x),
-                       static_cast<const float*>(router_w), bias, T, d, E, K, topk_ids, topk_w);
+    launch_router_act<float>(x, router_w, bias, T, d, E, K, topk_ids, topk_w, stream);
   }
   return hipGetLastError();
 }
