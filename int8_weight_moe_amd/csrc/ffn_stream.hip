@@ -45,10 +45,15 @@ namespace {
 #ifndef MOE_STREAM_NG_DN
 #define MOE_STREAM_NG_DN 4
 #endif
-// down-pass groups per wave of the 64-row variant (its accumulators and
-// activation ring are four times larger)
+// groups per wave of the 64-row variant: each wave re-reads its rows'
+// activations from L2 for every step, so wider gate/up items halve that
+// traffic; the down pass, whose accumulators and activation ring are four
+// times larger, keeps fewer groups than in the 32-row variant
 #ifndef MOE_STREAM_NG_DN_WIDE
 #define MOE_STREAM_NG_DN_WIDE 2
+#endif
+#ifndef MOE_STREAM_NG_GU_WIDE
+#define MOE_STREAM_NG_GU_WIDE 2
 #endif
 #ifndef MOE_STREAM_P_DN
 #define MOE_STREAM_P_DN 4
@@ -311,7 +316,8 @@ __global__ __launch_bounds__(stream_block_waves(KS) * kWave) void ffn_stream_ker
 
 template <bool kGateUp, typename Act, bool kScaleBf16, int F, int RB, int KS>
 hipError_t launch_stream_pass_ks(const FfnArgs& a, long items, hipStream_t stream) {
-  constexpr int NG = kGateUp ? MOE_STREAM_NG_GU : (RB >= 4 ? MOE_STREAM_NG_DN_WIDE : MOE_STREAM_NG_DN);
+  constexpr int NG = kGateUp ? (RB >= 4 ? MOE_STREAM_NG_GU_WIDE : MOE_STREAM_NG_GU)
+                             : (RB >= 4 ? MOE_STREAM_NG_DN_WIDE : MOE_STREAM_NG_DN);
   constexpr int P = kGateUp ? MOE_STREAM_P_GU : MOE_STREAM_P_DN;
   const int N = kGateUp ? a.f : a.d;
   const int Kd = kGateUp ? a.d : a.f;
@@ -331,7 +337,8 @@ hipError_t launch_stream_pass_ks(const FfnArgs& a, long items, hipStream_t strea
 
 template <bool kGateUp, typename Act, bool kScaleBf16, int F, int RB>
 hipError_t launch_stream_pass_rb(const FfnArgs& a, hipStream_t stream) {
-  constexpr int NG = kGateUp ? MOE_STREAM_NG_GU : (RB >= 4 ? MOE_STREAM_NG_DN_WIDE : MOE_STREAM_NG_DN);
+  constexpr int NG = kGateUp ? (RB >= 4 ? MOE_STREAM_NG_GU_WIDE : MOE_STREAM_NG_GU)
+                             : (RB >= 4 ? MOE_STREAM_NG_DN_WIDE : MOE_STREAM_NG_DN);
   const int N = kGateUp ? a.f : a.d;
   const long items = (long)a.E * (N / (16 * NG));
   switch (choose_split(items, RB)) {
