@@ -40,7 +40,8 @@
  *     produces (see there). router_w [E, d] is row-major; scales
  *     s_gate, s_up [E, f], s_down [E, d] are row-major.
  *   - Slots: token t's k-th choice is slot s = t*K + k.
- *   - T = 0 is valid and enqueues nothing.
+ *   - T = 0 is valid and enqueues nothing; once the shape is valid, no
+ *     pointer is then checked (empty tensors may be NULL).
  */
 #ifndef MOE_INT8_H
 #define MOE_INT8_H

@@ -195,12 +195,12 @@ moe_status moe_route(const moe_shape* s, const void* x, const void* router_w, co
                      int32_t* topk_ids, float* topk_w, hipStream_t stream) {
   moe_status st = check_shape(s);
   if (st != MOE_OK) return st;
+  if (s->T == 0) return MOE_OK;   // nothing is read or written
   REQUIRE_PTR(x);
   REQUIRE_PTR(router_w);
   REQUIRE_PTR(topk_ids);
   REQUIRE_PTR(topk_w);
   if (router_bias && !aligned16(router_bias)) return fail(MOE_ERR_ALIGN, "router_bias is not 16-byte aligned");
-  if (s->T == 0) return MOE_OK;
   const hipError_t e = moe::launch_router(x, router_w, router_bias, s->T, s->d, s->E, s->K,
                                           s->act_dtype == MOE_BF16, topk_ids, topk_w, stream);
   if (e != hipSuccess) return hip_fail(e, "router launch");
@@ -211,11 +211,11 @@ moe_status moe_permute(const moe_shape* s, const int32_t* topk_ids, int32_t* exp
                        int32_t* sorted_slots, int32_t* slot_to_row, hipStream_t stream) {
   moe_status st = check_shape(s);
   if (st != MOE_OK) return st;
+  if (s->T == 0) return MOE_OK;   // nothing is read or written
   REQUIRE_PTR(topk_ids);
   REQUIRE_PTR(expert_offsets);
   REQUIRE_PTR(sorted_slots);
   REQUIRE_PTR(slot_to_row);
-  if (s->T == 0) return MOE_OK;
   const hipError_t e = moe::launch_permute(topk_ids, s->T * s->K, s->E, expert_offsets, sorted_slots,
                                            slot_to_row, stream);
   if (e != hipSuccess) return hip_fail(e, "permute launch");
@@ -230,6 +230,7 @@ moe_status moe_expert_ffn(const moe_shape* s, const void* x, const int32_t* expe
   if (st != MOE_OK) return st;
   st = check_ffn(s);
   if (st != MOE_OK) return st;
+  if (s->T == 0) return MOE_OK;   // nothing is read or written
   REQUIRE_PTR(x);
   REQUIRE_PTR(expert_offsets);
   REQUIRE_PTR(sorted_slots);
@@ -244,7 +245,6 @@ moe_status moe_expert_ffn(const moe_shape* s, const void* x, const int32_t* expe
   const size_t need = ffn_ws_bytes(s);
   if (workspace_bytes < need)
     return fail(MOE_ERR_WORKSPACE, "workspace_bytes=%zu < required %zu", workspace_bytes, need);
-  if (s->T == 0) return MOE_OK;
   const moe::FfnArgs a = ffn_args(s, x, expert_offsets, sorted_slots, w_gate, w_up, w_down, s_gate, s_up, s_down,
                                   y_rows, static_cast<__bf16*>(workspace));
   st = run_gate_up(s, a, stream);
@@ -259,6 +259,7 @@ moe_status moe_expert_gate_up(const moe_shape* s, const void* x, const int32_t* 
   if (st != MOE_OK) return st;
   st = check_ffn(s);
   if (st != MOE_OK) return st;
+  if (s->T == 0) return MOE_OK;   // nothing is read or written
   REQUIRE_PTR(x);
   REQUIRE_PTR(expert_offsets);
   REQUIRE_PTR(sorted_slots);
@@ -267,7 +268,6 @@ moe_status moe_expert_gate_up(const moe_shape* s, const void* x, const int32_t* 
   REQUIRE_SCALE(s, s_gate);
   REQUIRE_SCALE(s, s_up);
   REQUIRE_PTR(h);
-  if (s->T == 0) return MOE_OK;
   const moe::FfnArgs a = ffn_args(s, x, expert_offsets, sorted_slots, w_gate, w_up, nullptr, s_gate, s_up, nullptr,
                                   nullptr, static_cast<__bf16*>(h));
   return run_gate_up(s, a, stream);
@@ -279,12 +279,12 @@ moe_status moe_expert_down(const moe_shape* s, const void* h, const int32_t* exp
   if (st != MOE_OK) return st;
   st = check_ffn(s);
   if (st != MOE_OK) return st;
+  if (s->T == 0) return MOE_OK;   // nothing is read or written
   REQUIRE_PTR(h);
   REQUIRE_PTR(expert_offsets);
   REQUIRE_PTR(w_down);
   REQUIRE_SCALE(s, s_down);
   REQUIRE_PTR(y_rows);
-  if (s->T == 0) return MOE_OK;
   const moe::FfnArgs a = ffn_args(s, nullptr, expert_offsets, nullptr, nullptr, nullptr, w_down, nullptr, nullptr,
                                   s_down, y_rows, static_cast<__bf16*>(const_cast<void*>(h)));
   return run_down(s, a, stream);
@@ -294,11 +294,11 @@ moe_status moe_combine(const moe_shape* s, const float* y_rows, const int32_t* s
                        const float* topk_w, void* y, hipStream_t stream) {
   moe_status st = check_shape(s);
   if (st != MOE_OK) return st;
+  if (s->T == 0) return MOE_OK;   // nothing is read or written
   REQUIRE_PTR(y_rows);
   REQUIRE_PTR(slot_to_row);
   REQUIRE_PTR(topk_w);
   REQUIRE_PTR(y);
-  if (s->T == 0) return MOE_OK;
   const hipError_t e = moe::launch_combine(y_rows, slot_to_row, topk_w, s->T, s->d, s->K,
                                            s->act_dtype == MOE_BF16, y, stream);
   if (e != hipSuccess) return hip_fail(e, "combine launch");
@@ -313,6 +313,7 @@ moe_status moe_forward(const moe_shape* s, const void* x, const void* router_w, 
   if (st != MOE_OK) return st;
   st = check_ffn(s);
   if (st != MOE_OK) return st;
+  if (s->T == 0) return MOE_OK;   // nothing is read or written
   REQUIRE_PTR(x);
   REQUIRE_PTR(router_w);
   REQUIRE_PTR(w_gate);
@@ -329,7 +330,6 @@ moe_status moe_forward(const moe_shape* s, const void* x, const void* router_w, 
   const WsLayout L = forward_layout(s);
   if (workspace_bytes < L.total)
     return fail(MOE_ERR_WORKSPACE, "workspace_bytes=%zu < required %zu", workspace_bytes, L.total);
-  if (s->T == 0) return MOE_OK;
 
   char* ws = static_cast<char*>(workspace);
   int32_t* ids = topk_ids_out ? topk_ids_out : reinterpret_cast<int32_t*>(ws + L.ids);
@@ -372,6 +372,7 @@ moe_status moe_mlp_forward(const moe_shape* s, const void* x, const void* w_gate
   st = check_ffn(s);
   if (st != MOE_OK) return st;
   if (s->E != 1 || s->K != 1) return fail(MOE_ERR_SHAPE, "the dense MLP needs E = K = 1 (E=%d, K=%d)", s->E, s->K);
+  if (s->T == 0) return MOE_OK;   // nothing is read or written
   REQUIRE_PTR(x);
   REQUIRE_PTR(w_gate);
   REQUIRE_PTR(w_up);
@@ -384,7 +385,6 @@ moe_status moe_mlp_forward(const moe_shape* s, const void* x, const void* w_gate
   const WsLayout L = forward_layout(s);
   if (workspace_bytes < L.total)
     return fail(MOE_ERR_WORKSPACE, "workspace_bytes=%zu < required %zu", workspace_bytes, L.total);
-  if (s->T == 0) return MOE_OK;
   char* ws = static_cast<char*>(workspace);
   float* wts = reinterpret_cast<float*>(ws + L.w);
   int32_t* offsets = reinterpret_cast<int32_t*>(ws + L.offsets);

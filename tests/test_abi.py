@@ -120,6 +120,12 @@ def test_empty_input_enqueues_nothing(lib):
     assert lib.moe_combine(ctypes.byref(s), A, A, A, A, None) == 0
     assert lib.moe_forward(ctypes.byref(s), A, A, None, A, A, A, A, A, A, A, None, None, A,
                            ctypes.c_size_t(need.value), None) == 0
+    # empty tensors may be NULL: nothing is read or written
+    assert lib.moe_route(ctypes.byref(s), None, None, None, None, None, None) == 0
+    assert lib.moe_forward(ctypes.byref(s), *([None] * 13), ctypes.c_size_t(0), None) == 0
+    # an invalid shape is still reported
+    bad = _shape(T=0, d=100)
+    assert lib.moe_forward(ctypes.byref(bad), *([None] * 13), ctypes.c_size_t(0), None) == 2
 
 
 def test_mlp_validation(lib):
@@ -160,7 +166,7 @@ def test_weight_format_rules(lib):
                            ctypes.c_size_t(n.value), None) == 0
     # int8 and fp8 weights need their scales
     for fmt in (0, 2):
-        s = _shape(T=0, weight_fmt=fmt)
+        s = _shape(T=8, weight_fmt=fmt)
         assert lib.moe_forward(ctypes.byref(s), A, A, None, A, A, A, None, A, A, A, None, None, A,
                                ctypes.c_size_t(1 << 30), None) == 1
     # the comparator encodings run with bf16 activations only

@@ -9,8 +9,8 @@ import pytest
 import torch
 
 import workloads
-from int8_weight_moe_amd import (MoeError, moe_combine, moe_expert_ffn, moe_forward, moe_pack_rows, moe_permute,
-                                 moe_quantize_rows, moe_route)
+from int8_weight_moe_amd import (MoeError, moe_combine, moe_expert_ffn, moe_forward, moe_mlp_forward, moe_pack_rows,
+                                 moe_permute, moe_quantize_rows, moe_route)
 from int8_weight_moe_amd._lib import MOE_PATH_AUTO, MOE_PATH_STREAM, MOE_PATH_TILED
 from oracle import moe as omoe
 from oracle import quant as oquant
@@ -200,6 +200,9 @@ def test_combine_matches_oracle(T, d, K, act):
     (40, 128, 192, 8, 8, "bf16", "bf16", None),      # K = E: dense mixture
     (33, 192, 256, 1, 1, "bf16", "bf16", None),      # E = K = 1: dense int8 MLP
     (100, 128, 128, 16, 2, "bf16", "bf16", [0.0] * 5 + [100.0] + [0.0] * 10),  # hot expert 5 in every token
+    (50, 128, 128, 64, 8, "bf16", "bf16", None),     # the largest E and K
+    (5, 65536, 64, 2, 1, "bf16", "bf16", None),      # the largest d
+    (3, 64, 131072, 2, 2, "bf16", "f32", None),      # the largest f
 ])
 def test_forward_matches_oracle(path, T, d, f, E, K, act, scale, bias):
     w, x, wr, b, W = _case(T, d, f, E, K, act, scale, bias=bias, seed=9)
@@ -252,3 +255,23 @@ def test_library_errors_raise():
     wr = torch.zeros((16, 100), dtype=torch.bfloat16, device="cuda")
     with pytest.raises(MoeError):
         moe_route(x, wr, None, 2)
+
+
+@pytest.mark.parametrize("path", [MOE_PATH_AUTO, MOE_PATH_STREAM, MOE_PATH_TILED])
+def test_empty_batch(path):
+    """T = 0 through every call: empty outputs, nothing launched, no error."""
+    w, x, wr, _, W = _case(4, 128, 192, 8, 2, seed=2)
+    ex = experts_to_device(W, TDT["bf16"])
+    x0 = x[:0].cuda()
+    y, ids, gw = moe_forward(x0, wr.cuda(), None, ex, 2, path=path)
+    assert y.shape == (0, 128) and ids.shape == (0, 2) and gw.shape == (0, 2)
+    ids, gw = moe_route(x0, wr.cuda(), None, 2)
+    off, ss, s2r = moe_permute(ids, 8)
+    rows = moe_expert_ffn(x0, off, ss, ex, 2, path=path)
+    y2 = moe_combine(rows, s2r, gw, torch.bfloat16)
+    torch.cuda.synchronize()
+    assert rows.shape == (0, 128) and y2.shape == (0, 128)
+    _, _, _, _, W1 = _case(4, 128, 192, 1, 1, seed=2)
+    y3 = moe_mlp_forward(x0, experts_to_device(W1, TDT["bf16"]), path=path)
+    torch.cuda.synchronize()
+    assert y3.shape == (0, 128)
