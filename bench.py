@@ -289,6 +289,31 @@ def cpu_baseline(w, x_host, layer, src, n_experts):
             "step_ms_estimate": round(est * 1e3, 1)}
 
 
+def vendor_gemm_reference(wp, dev, iters=10):
+    """Context for the MFMA roofline: the vendor library's plain bf16 GEMM (torch.matmul ->
+    hipBLASLt) on the prefill contractions as single dense GEMMs (no grouping, no
+    dequantization): [S, d] x [d, 2f] and [S, f] x [f, d]. Returns TFLOP/s of each."""
+    import torch
+    S = wp.T * wp.K
+    out = {}
+    for name, (M, N, K) in (("gate_up", (S, 2 * wp.f, wp.d)), ("down", (S, wp.d, wp.f))):
+        a = torch.randn(M, K, device=dev, dtype=torch.bfloat16)
+        b = torch.randn(N, K, device=dev, dtype=torch.bfloat16)
+        c = a @ b.t()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(iters):
+            c = a @ b.t()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / iters
+        out[name + "_tflops"] = round(2.0 * M * N * K / (ms * 1e-3) / 1e12, 1)
+        del a, b, c
+    torch.cuda.empty_cache()
+    return out
+
+
 def measure_prefill(layer, wp, xp, bias, args, dense, wfmt="int8"):
     """Step time, kernel split and roofline of the sibling prefill workload on this layer."""
     from int8_weight_moe_amd._lib import MOE_PATH_AUTO
@@ -382,6 +407,8 @@ def main():
             if wp.has_bias:
                 prefill_bias = torch.tensor([wp.hot_bias, wp.hot_bias] + [0.0] * (w.E - 2), device=dev)
             result["prefill"] = measure_prefill(layer, wp, prefill_x, prefill_bias, args, dense)
+            result["prefill"]["vendor_bf16_gemm"] = vendor_gemm_reference(wp, dev)
+            log(f"vendor bf16 GEMM reference (hipBLASLt, ungrouped): {result['prefill']['vendor_bf16_gemm']}")
 
     # weight-encoding comparators: the same layer, inputs and schedule choice
     if not args.no_compare and w.act == "bf16" and w.weight_src == "bf16":
