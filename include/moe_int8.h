@@ -62,7 +62,7 @@ enum {
   MOE_ERR_DTYPE = 3,       /* unknown dtype code */
   MOE_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned */
   MOE_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required */
-  MOE_ERR_UNSUPPORTED = 6, /* valid request this build does not implement */
+  MOE_ERR_UNSUPPORTED = 6, /* valid request the library does not support */
   MOE_ERR_HIP = 7          /* a HIP runtime call failed */
 };
 
@@ -144,8 +144,8 @@ moe_status moe_permute(const moe_shape* shape, const int32_t* topk_ids,
 /* Expert SwiGLU FFNs on the permuted rows (the ExpertsInt8 contraction).
  *   x              [T, d] act_dtype (row of sorted row r is token sorted_slots[r] / K)
  *   expert_offsets [E+1], sorted_slots [T*K] from moe_permute
- *   w_gate, w_up   [E, f, d] int8;  w_down [E, d, f] int8 -- tiled layout (moe_pack_rows)
- *   s_gate, s_up   [E, f] scale_dtype;  s_down [E, d] scale_dtype
+ *   w_gate, w_up   [E, f, d];  w_down [E, d, f] -- shape->weight_fmt encoding, tiled layout (moe_pack_rows)
+ *   s_gate, s_up   [E, f] scale_dtype;  s_down [E, d] scale_dtype (unused for MOE_W_BF16)
  *   y_rows         [T*K, d] fp32 out: row r = output of sorted row r's expert
  *   workspace      >= moe_ffn_workspace_size bytes (holds h)
  * Rows past off[E] are left untouched. */
@@ -188,8 +188,8 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const void* router
  * Improvements": ExpertsInt8 quantizes the MoE *and* the MLP weights). An MLP
  * layer is the MoE layer with one expert used by every token with weight 1:
  *   y = s_d * (q_d . h),  h = silu(s_g * (q_g . x)) * (s_u * (q_u . x)).
- * shape->E and shape->K must be 1; no router. Same kernels and layouts as the
- * MoE calls (weights in the tiled int8 layout), same tolerance.
+ * shape->E and shape->K must be 1; no router. Same kernels, weight encodings
+ * and layouts as the MoE calls, same tolerance.
  *   y [T, d] act_dtype out; workspace >= moe_mlp_workspace_size bytes. */
 moe_status moe_mlp_workspace_size(const moe_shape* shape, size_t* bytes);
 moe_status moe_mlp_forward(const moe_shape* shape, const void* x,
