@@ -23,6 +23,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import statistics
 import sys
 import time
@@ -196,11 +197,20 @@ def time_stages(layer, x, path, steps, warmup, dense=False):
     return out
 
 
+def _code_only(text):
+    """Source text without comments and blank space, so that edits to comments
+    do not invalidate the counter measurements tied to the code."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return " ".join(text.split())
+
+
 def kernel_hash():
+    """Hash of the code of the FFN kernels (comments and spacing excluded)."""
     hsh = hashlib.sha256()
     for f in ("ffn_stream.hip", "ffn_tiled.hip", "device_common.h"):
-        with open(os.path.join(ROOT, "int8_weight_moe_amd", "csrc", f), "rb") as fh:
-            hsh.update(fh.read())
+        with open(os.path.join(ROOT, "int8_weight_moe_amd", "csrc", f)) as fh:
+            hsh.update(_code_only(fh.read()).encode())
     return hsh.hexdigest()[:16]
 
 

@@ -13,7 +13,10 @@
 //   - the int8 codes become bf16 in registers (exact) and feed 16x16x32 bf16
 //     MFMA, with the channels as MFMA rows and the tokens as MFMA columns;
 //   - a 64-wide step is two MFMAs: code bytes 0-7 of each lane pair with
-//     activation elements 0-7 of the same lane group, bytes 8-15 with 8-15.
+//     activation elements 0-7 of the same lane group, bytes 8-15 with 8-15;
+//   - the comparator encodings (WFormat: bf16 weights, fp8 codes) change only
+//     how a lane's pieces become the two operands and which activation
+//     elements pair with them.
 // Items are numbered over the experts that received rows only, so the grid
 // has no idle waves for untouched experts.
 // With few experts (a dense MLP layer: one) there are too few items to keep

@@ -7,10 +7,13 @@
 //                 epilogue h = silu(s_g * g) * (s_u * u) -> bf16;
 //   down pass:    C = H_e (BM rows of h) times W_down_e channels n0..n0+BN,
 //                 epilogue y_rows = s_d * acc -> fp32.
-// Per 64-wide reduction step the workgroup stages the activation tile (bf16)
-// and the weight tile in LDS; the weight tile arrives as int8 (half the bytes
-// of bf16 -- the ExpertsInt8 point) and is converted to bf16 exactly on its
-// way into LDS, once per workgroup. The LDS tiles are double buffered, so the
+// Two kernels: the register-staged one below (fp32 activations, or tensors
+// past 32-bit byte offsets) and the direct-to-LDS one after it (bf16
+// activations: every prefill workload). In the register-staged kernel, per
+// 64-wide reduction step the workgroup stages the activation tile (bf16) and
+// the weight tile in LDS; the weight tile arrives as int8 (half the bytes of
+// bf16 -- the ExpertsInt8 point) and is converted to bf16 exactly on its way
+// into LDS, once per workgroup. The LDS tiles are double buffered, so the
 // global loads of step k+1 are in flight while step k's MFMAs run; one barrier
 // per step. Rows are 128 bytes in LDS with the 16-byte chunks XOR-swizzled by
 // (row mod 8), so the fragment reads (16 rows at one chunk) and the tile writes
@@ -279,20 +282,26 @@ __global__ __launch_bounds__(WM * WN * kWave) void ffn_tiled_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// bf16-activation kernel: operands reach LDS by direct global->LDS loads.
+// bf16-activation kernel (the one prefill runs): operands reach LDS by direct
+// global->LDS loads.
 //
-// Same tiles and tile order as above, but nothing is staged in registers: each
-// wave issues 16-byte global_load_lds instructions that write a contiguous
-// 1 KiB of LDS. A 3-stage LDS ring keeps the loads of the next two reduction
-// steps in flight while one is computed (per step: wait for this step's loads
-// with an explicit vmcnt, one barrier, issue the step two ahead, compute).
-//   activations: 256 rows x 128 bytes per step; instruction c of the tile
+// Same tile order as above; the tile is BM x BN = 128 x 256 (gate/up: 128
+// channels of each matrix) over WM x WN = 1 x 4 waves, so a wave owns all 128
+// rows and 64 of the columns and no weight fragment is read by two waves.
+// Nothing is staged in registers: each wave issues 16-byte global_load_lds
+// instructions that write a contiguous 1 KiB of LDS. A STAGES-deep LDS ring
+// (2: 64 KiB, so two workgroups share a CU) keeps the loads of the next step
+// in flight while one is computed (per step: wait for this step's loads with
+// an explicit vmcnt, one barrier, issue the step STAGES-1 ahead, compute).
+//   activations: BM rows x 128 bytes per step; instruction c of the tile
 //     covers rows 8c..8c+7, lane l writes row 8c + l/8, 16-byte chunk l%8,
 //     and fetches the logical chunk (l%8) ^ (row%8) -- so the tile lands in LDS
 //     already XOR-swizzled and the fragment reads stay conflict-free;
-//   weights: the tiled int8 layout is copied block for block (1 KiB per
-//     16-channel group and step) and stays int8 in LDS (half the bytes); a
-//     fragment is one 8-byte LDS read, converted to bf16 exactly in registers.
+//   weights: the tiled layout is copied block for block (1 KiB per 16-channel
+//     group and step; two blocks for the bf16 comparator) and stays in its
+//     encoding in LDS (int8: half the bytes of bf16); a lane reads one 16-byte
+//     piece per block and converts it in registers into the step's two MFMA
+//     operands (WFormat).
 // Rows past the expert's segment and channels past N load valid in-range
 // data whose results are never stored.
 // One 16-byte-per-lane global->LDS load: lane l reads base + voff (its own
