@@ -52,9 +52,27 @@ def test_roofline_records():
     assert p["achieved"] == pytest.approx(a["gate_up_flops"] / 3000e-6 / 1e12, abs=0.05)   # rounded to 0.1
 
 
-def test_counter_lookup_follows_the_kernel_code():
-    # the committed counter summaries match the current kernels, and the key ignores comments
-    assert bench.measured_traffic("mini-decode", "gate_up") is not None
+def test_counter_lookup_follows_the_kernel_code(tmp_path, monkeypatch):
+    h = bench.kernel_hash()
+    prof = tmp_path / "profiles"
+    prof.mkdir()
+    (prof / "traffic_gate_up_wl.txt").write_text(f"# note\nhbm_bytes_per_launch=123\nkernel_source_hash={h}\n")
+    (prof / "traffic_gate_up_old.txt").write_text("hbm_bytes_per_launch=123\nkernel_source_hash=0000\n")
+    csrc = tmp_path / "int8_weight_moe_amd" / "csrc"
+    csrc.mkdir(parents=True)
+    for f in ("ffn_stream.hip", "ffn_tiled.hip", "device_common.h"):
+        (csrc / f).write_text(open(os.path.join(ROOT, "int8_weight_moe_amd", "csrc", f)).read())
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    assert bench.measured_traffic("wl", "gate_up") == 123.0
+    assert bench.measured_traffic("old", "gate_up") is None          # stale counters are not reported
+    assert bench.measured_traffic("missing", "gate_up") is None
+    # a comment edit keeps the key, a code edit changes it
+    with open(csrc / "ffn_tiled.hip", "a") as fh:
+        fh.write("\n// a new comment\n")
+    assert bench.kernel_hash() == h
+    with open(csrc / "ffn_tiled.hip", "a") as fh:
+        fh.write("\nint extra_symbol;\n")
+    assert bench.kernel_hash() != h
     code = "int a; // note\n/* block\n comment */ int  b;"
     assert bench._code_only(code) == bench._code_only("int a;\nint b;")
     assert bench._code_only(code) != bench._code_only("int a; int c;")
