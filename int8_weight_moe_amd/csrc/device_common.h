@@ -37,6 +37,30 @@ __device__ __forceinline__ uint4 load_nt16(const void* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// ---------------------------------------------------------------- direct global->LDS loads
+// One 16-byte-per-lane global->LDS load: lane l reads base + voff (its own
+// 32-bit byte offset) and its 16 bytes land at LDS byte address lds + 16*l.
+// Written as inline asm with no output register and a memory clobber: the
+// compiler's own handling of these loads waits for all of them before every
+// LDS read, which would drain the ring; here the only waits are the explicit
+// vmcnt counts of the pipeline. m0 (the LDS base of the load) is set right
+// before each load; nothing else in the FFN kernels uses m0. `base` and `lds`
+// are wave-uniform.
+__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff), "s"(base) : "memory");
+}
+
+// LDS byte address of a __shared__ object: the low 32 bits of its generic
+// address (the shared aperture base has zero low bits).
+template <typename T>
+__device__ __forceinline__ uint32_t lds_addr(const T* p) {
+  return (uint32_t)(uintptr_t)p;
+}
+
+// s_waitcnt immediate (gfx9 encoding): wait until at most `vm` vector-memory
+// operations are outstanding and all LDS operations have completed.
+constexpr int waitcnt_vm_lgkm0(int vm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4); }
+
 // ---------------------------------------------------------------- conversions
 // Eight int8 codes (two dwords, byte 0 first) -> eight bf16 values. Exact: a
 // code has at most 8 significant bits. Compiles to one sign-extending

@@ -80,6 +80,17 @@ namespace {
 #ifndef MOE_STREAM_PA_WIDE
 #define MOE_STREAM_PA_WIDE 2
 #endif
+// the 64-row gate/up pass shares its activations through LDS (1) or not (0);
+// ring depth of that kernel; workgroups it aims for (one per CU)
+#ifndef MOE_STREAM_SHARED_GU
+#define MOE_STREAM_SHARED_GU 1
+#endif
+#ifndef MOE_STREAM_P_SHARED
+#define MOE_STREAM_P_SHARED 6
+#endif
+#ifndef MOE_STREAM_SHARED_MIN_WGS
+#define MOE_STREAM_SHARED_MIN_WGS 256
+#endif
 constexpr int kStreamWaves = MOE_STREAM_WAVES;
 
 constexpr int ring_gcd(int a, int b) { return b == 0 ? a : ring_gcd(b, a % b); }
@@ -317,6 +328,192 @@ __global__ __launch_bounds__(stream_block_waves(KS) * kWave) void ffn_stream_ker
   }
 }
 
+// Gate/up pass of the 64-row variant with the activations shared through LDS.
+// With many rows per expert (a dense MLP layer at decode) every wave of
+// ffn_stream_kernel re-reads the rows' activations from L2 for each step,
+// which costs more vector-memory traffic than the weights it streams. Here a
+// workgroup of W waves holds W consecutive items of one expert (no reduction
+// split): per 64-wide step its waves copy the 64-row activation tile (8 KiB
+// bf16) once into a P-deep LDS ring with direct-to-LDS loads, while each wave
+// streams its own weight blocks into a P-deep register ring; one barrier per
+// step. The tile lands XOR-swizzled by row as in the tiled kernel; each
+// item's MFMAs run in the same order as in ffn_stream_kernel without a
+// reduction split.
+// Loads per step and wave: NG*2*PPS weight loads, then its share of the 8
+// activation DMAs. Before step s the activations of step s must have landed
+// while the loads of steps s+1..s+P-2 may still be in flight.
+template <bool kScaleBf16, int F, int NG, int W, int P>
+__global__ __launch_bounds__(W * kWave) void ffn_stream_shared_gu_kernel(
+    const __bf16* __restrict__ X, const int32_t* __restrict__ sorted_slots, int topk,
+    const int8_t* __restrict__ W0, const int8_t* __restrict__ W1, const void* __restrict__ S0,
+    const void* __restrict__ S1, const int32_t* __restrict__ offsets, int E, int N, int Kd,
+    __bf16* __restrict__ out) {
+  constexpr int NMAT = 2;
+  constexpr int RB = 4;                      // 16-row blocks per pass
+  constexpr int ROWS = 16 * RB;
+  using WF = WFormat<F>;
+  constexpr int PPS = WF::kPieces;
+  constexpr int STAGE = ROWS * 128;          // one step's activation tile
+  constexpr int A_TOT = STAGE / 1024;        // its 1 KiB DMA instructions, dealt round-robin to the waves
+  constexpr int A_MAX = (A_TOT + W - 1) / W;
+  constexpr int A_MIN = A_TOT / W;
+  constexpr int NWI = NG * NMAT * PPS;       // weight loads per wave and step
+  static_assert((P - 2) * (NWI + A_MAX) <= 63, "the vmcnt field holds at most 63");
+  __shared__ __attribute__((aligned(1024))) uint8_t act[P][STAGE];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int li = lane & 15;
+  const int lg = lane >> 4;
+
+  // ---- workgroup -> (expert among the touched ones, W consecutive items)
+  const int gpe = N / (16 * NG);
+  const int wg_per_e = gpe / W;
+  const int te = blockIdx.x / wg_per_e;
+  const int grp = (blockIdx.x - te * wg_per_e) * W + wave;
+  int e = -1, row0 = 0, nrows = 0;
+  {
+    int seen = 0;
+    for (int x = 0; x < E; ++x) {
+      const int o0 = offsets[x], o1 = offsets[x + 1];
+      if (o1 > o0) {
+        if (seen == te) {
+          e = x;
+          row0 = o0;
+          nrows = o1 - o0;
+          break;
+        }
+        ++seen;
+      }
+    }
+  }
+  if (e < 0) return;   // the same for every wave of the workgroup
+
+  const int ch_base = grp * 16 * NG;
+  const int8_t* wp[NG][NMAT];
+  float4 sc[NG][NMAT];
+#pragma unroll
+  for (int ng = 0; ng < NG; ++ng) {
+    const long group = ((long)e * N + ch_base + ng * 16) >> 4;
+    const long off = group * (long)(Kd >> 6) * (1024 * PPS) + 16 * lane;
+    wp[ng][0] = W0 + off;
+    wp[ng][1] = W1 + off;
+    const long ch = (long)e * N + ch_base + ng * 16 + 4 * lg;
+    sc[ng][0] = make_float4(1.f, 1.f, 1.f, 1.f);
+    sc[ng][1] = sc[ng][0];
+    if constexpr (WF::kScaled) {
+      sc[ng][0] = load_scale4<kScaleBf16>(S0, ch);
+      sc[ng][1] = load_scale4<kScaleBf16>(S1, ch);
+    }
+  }
+  const int nsteps = Kd >> 6;
+
+  for (int p0 = 0; p0 < nrows; p0 += ROWS) {
+    const int prow = min(ROWS, nrows - p0);
+    const int nrb = (prow + 15) >> 4;
+    // this wave's activation DMAs: tile instruction c = wave + W*j covers rows
+    // 8c..8c+7; lane l writes row 8c + l/8, chunk slot l%8, fetched from the
+    // logical chunk slot ^ (row % 8); rows past the pass re-read row 0
+    uint32_t a_off[A_MAX];
+#pragma unroll
+    for (int j = 0; j < A_MAX; ++j) {
+      const int c = min(wave + W * j, A_TOT - 1);
+      const int r = 8 * c + (lane >> 3);
+      const int rr = (r < prow) ? r : 0;
+      const uint32_t src_row = (uint32_t)(sorted_slots[row0 + p0 + rr] / topk);
+      const int chunk = (lane & 7) ^ (r & 7);
+      a_off[j] = (src_row * (uint32_t)Kd + (uint32_t)(chunk * 8)) * 2u;
+    }
+
+    f32x4 acc[RB][NG][NMAT];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int ng = 0; ng < NG; ++ng)
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m) acc[rb][ng][m] = f32x4{0.f, 0.f, 0.f, 0.f};
+    uint4 bw[P][NG][NMAT][PPS];
+
+    auto issue = [&](int t, int st) {
+#pragma unroll
+      for (int ng = 0; ng < NG; ++ng)
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+          for (int q = 0; q < PPS; ++q) bw[st][ng][m][q] = load_nt16(wp[ng][m] + ((long)t * PPS + q) * 1024);
+#pragma unroll
+      for (int j = 0; j < A_MAX; ++j)
+        if (wave + W * j < A_TOT)
+          dma16(X, a_off[j] + (uint32_t)t * 128u, lds_addr(&act[st][0]) + (wave + W * j) * 1024);
+    };
+    auto compute = [&](int st) {
+      bf16x8 xf[RB][2];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        if (rb < nrb) {
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            const int row = rb * 16 + li;
+            const int chunk = ((WF::kActLane * lg + WF::kActSecond * ks) >> 3) ^ (row & 7);
+            xf[rb][ks] = *reinterpret_cast<const bf16x8*>(&act[st][row * 128 + chunk * 16]);
+          }
+        }
+      }
+#pragma unroll
+      for (int ng = 0; ng < NG; ++ng) {
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m) {
+          bf16x8 w_lo, w_hi;
+          WF::operands(bw[st][ng][m], w_lo, w_hi);
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) {
+            if (rb < nrb) {
+              acc[rb][ng][m] = mfma_bf16(w_lo, xf[rb][0], acc[rb][ng][m]);
+              acc[rb][ng][m] = mfma_bf16(w_hi, xf[rb][1], acc[rb][ng][m]);
+            }
+          }
+        }
+      }
+    };
+
+#pragma unroll
+    for (int t = 0; t < P - 1; ++t) issue(min(t, nsteps - 1), t);
+    for (int s0 = 0; s0 < nsteps; s0 += P) {
+#pragma unroll
+      for (int j = 0; j < P; ++j) {
+        if (s0 + j < nsteps) {   // the same for every wave
+          __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0((P - 2) * (NWI + A_MIN)));
+          __builtin_amdgcn_s_barrier();
+          issue(min(s0 + j + P - 1, nsteps - 1), (j + P - 1) % P);
+          compute(j);
+        }
+      }
+    }
+    // no load may still be writing the ring when it is reused or the waves exit
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+    __builtin_amdgcn_s_barrier();
+
+    // ---- epilogue (as ffn_stream_kernel's gate/up pass)
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const int r = p0 + rb * 16 + li;
+      if (rb < nrb && r < nrows) {
+        const long orow = (long)(row0 + r) * N;
+#pragma unroll
+        for (int ng = 0; ng < NG; ++ng) {
+          const int ch = ch_base + ng * 16 + 4 * lg;
+          const float sgv[4] = {sc[ng][0].x, sc[ng][0].y, sc[ng][0].z, sc[ng][0].w};
+          const float suv[4] = {sc[ng][1].x, sc[ng][1].y, sc[ng][1].z, sc[ng][1].w};
+          bf16x4 hv;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) hv[q] = (__bf16)(silu(acc[rb][ng][0][q] * sgv[q]) * (acc[rb][ng][1][q] * suv[q]));
+          *reinterpret_cast<bf16x4*>(out + orow + ch) = hv;
+        }
+      }
+    }
+  }
+}
+
 template <bool kGateUp, typename Act, bool kScaleBf16, int F, int RB, int KS>
 hipError_t launch_stream_pass_ks(const FfnArgs& a, long items, hipStream_t stream) {
   constexpr int NG = kGateUp ? (RB >= 4 ? MOE_STREAM_NG_GU_WIDE : MOE_STREAM_NG_GU)
@@ -352,12 +549,50 @@ hipError_t launch_stream_pass_rb(const FfnArgs& a, hipStream_t stream) {
   }
 }
 
+template <bool kScaleBf16, int F, int W>
+hipError_t launch_stream_shared_gu_w(const FfnArgs& a, hipStream_t stream) {
+  constexpr int NG = MOE_STREAM_NG_GU_WIDE;
+  const int gpe = a.f / (16 * NG);
+  const dim3 grid((unsigned)((long)a.E * (gpe / W)));
+  hipLaunchKernelGGL((ffn_stream_shared_gu_kernel<kScaleBf16, F, NG, W, MOE_STREAM_P_SHARED>), grid,
+                     dim3(W * kWave), 0, stream, static_cast<const __bf16*>(a.x), a.sorted_slots, a.K, a.w_gate,
+                     a.w_up, a.s_gate, a.s_up, a.offsets, a.E, a.f, a.d, a.h);
+  return hipGetLastError();
+}
+
+// Waves (items) per workgroup of the shared-activation gate/up pass: the most
+// of 4, 3, 2 that divides the items of an expert and still gives every CU a
+// workgroup; 2 always divides (f is a multiple of 64).
+int shared_gu_waves(int E, int f) {
+  const int gpe = f / (16 * MOE_STREAM_NG_GU_WIDE);
+  for (int w = 4; w >= 2; --w)
+    if (gpe % w == 0 && (long)E * (gpe / w) >= MOE_STREAM_SHARED_MIN_WGS) return w;
+  return 2;
+}
+
+template <bool kScaleBf16, int F>
+hipError_t launch_stream_shared_gu(const FfnArgs& a, hipStream_t stream) {
+  switch (shared_gu_waves(a.E, a.f)) {
+    case 4: return launch_stream_shared_gu_w<kScaleBf16, F, 4>(a, stream);
+    case 3: return launch_stream_shared_gu_w<kScaleBf16, F, 3>(a, stream);
+    default: return launch_stream_shared_gu_w<kScaleBf16, F, 2>(a, stream);
+  }
+}
+
 // Rows per pass: 16*RB. More than 32 rows per expert on average (a dense MLP
 // layer, or a hot expert at decode) takes the 64-row variant so the weights
 // are streamed once; otherwise the 32-row variant keeps more waves resident.
+// The 64-row gate/up pass with bf16 activations shares them through LDS when
+// their byte offsets fit 32 bits.
 template <bool kGateUp, typename Act, bool kScaleBf16, int F>
 hipError_t launch_stream_pass(const FfnArgs& a, hipStream_t stream) {
-  if ((long)a.S > 32L * a.E) return launch_stream_pass_rb<kGateUp, Act, kScaleBf16, F, 4>(a, stream);
+  if ((long)a.S > 32L * a.E) {
+    if constexpr (kGateUp && sizeof(Act) == 2) {
+      if (MOE_STREAM_SHARED_GU && (uint64_t)a.T * a.d * 2 < (1ull << 32))
+        return launch_stream_shared_gu<kScaleBf16, F>(a, stream);
+    }
+    return launch_stream_pass_rb<kGateUp, Act, kScaleBf16, F, 4>(a, stream);
+  }
   return launch_stream_pass_rb<kGateUp, Act, kScaleBf16, F, MOE_STREAM_RB>(a, stream);
 }
 

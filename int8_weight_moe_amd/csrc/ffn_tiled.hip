@@ -304,28 +304,7 @@ __global__ __launch_bounds__(WM * WN * kWave) void ffn_tiled_kernel(
 //     operands (WFormat).
 // Rows past the expert's segment and channels past N load valid in-range
 // data whose results are never stored.
-// One 16-byte-per-lane global->LDS load: lane l reads base + voff (its own
-// 32-bit byte offset) and its 16 bytes land at LDS byte address lds + 16*l.
-// Written as inline asm with no output register and a memory clobber: the
-// compiler's own handling of these loads waits for all of them before every
-// LDS read, which would drain the ring; here the only waits are the explicit
-// vmcnt counts of the pipeline. m0 (the LDS base of the load) is set right
-// before each load; nothing else in these kernels uses m0. `base` and `lds`
-// are wave-uniform.
-__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff), "s"(base) : "memory");
-}
-
-// LDS byte address of a __shared__ object: the low 32 bits of its generic
-// address (the shared aperture base has zero low bits).
-template <typename T>
-__device__ __forceinline__ uint32_t lds_addr(const T* p) {
-  return (uint32_t)(uintptr_t)p;
-}
-
-// s_waitcnt immediate (gfx9 encoding): wait until at most `vm` vector-memory
-// operations are outstanding and all LDS operations have completed.
-constexpr int waitcnt_vm_lgkm0(int vm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4); }
+// (dma16, lds_addr and waitcnt_vm_lgkm0 are in device_common.h)
 
 // Shape of the direct-to-LDS kernel: BM x BN tile, WM x WN waves, STAGES-deep ring.
 #ifndef MOE_DMA_BM
