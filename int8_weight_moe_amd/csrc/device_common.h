@@ -61,6 +61,61 @@ __device__ __forceinline__ uint32_t lds_addr(const T* p) {
 // operations are outstanding and all LDS operations have completed.
 constexpr int waitcnt_vm_lgkm0(int vm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4); }
 
+// ---------------------------------------------------------------- expert segment lookup
+// Both lookups read the E+1 segment offsets once, one expert per lane (E <= 64),
+// instead of walking the experts one dependent load at a time; every lane of
+// the wave returns the same (wave-uniform) answer.
+
+// Row tile `mt` of the expert-grouped rows, where expert x owns
+// ceil(count_x / BM) consecutive row tiles: its expert, first row and row
+// count. Returns false when mt is past the last tile.
+template <int BM>
+__device__ __forceinline__ bool find_row_tile(const int32_t* __restrict__ offsets, int E, int mt, int& e, int& row0,
+                                              int& nrows) {
+  const int lane = threadIdx.x & (kWave - 1);
+  int o0 = 0, o1 = 0;
+  if (lane < E) {
+    o0 = offsets[lane];
+    o1 = offsets[lane + 1];
+  }
+  const int tiles = (o1 - o0 + BM - 1) / BM;
+  int incl = tiles;   // inclusive scan of the tile counts over the lanes
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int v = __shfl_up(incl, d);
+    if (lane >= d) incl += v;
+  }
+  const int excl = incl - tiles;
+  const uint64_t hit = __ballot(lane < E && mt >= excl && mt < incl);
+  if (hit == 0) return false;
+  const int x = __builtin_amdgcn_readfirstlane(__ffsll((unsigned long long)hit) - 1);
+  e = x;
+  row0 = __builtin_amdgcn_readfirstlane(__shfl(o0, x) + (mt - __shfl(excl, x)) * BM);
+  nrows = __builtin_amdgcn_readfirstlane(min(BM, __shfl(o1, x) - row0));
+  return true;
+}
+
+// The te-th expert (in index order) among those with at least one row: its
+// index, first row and row count. Returns false when fewer experts have rows.
+__device__ __forceinline__ bool find_touched_expert(const int32_t* __restrict__ offsets, int E, int te, int& e,
+                                                    int& row0, int& nrows) {
+  const int lane = threadIdx.x & (kWave - 1);
+  int o0 = 0, o1 = 0;
+  if (lane < E) {
+    o0 = offsets[lane];
+    o1 = offsets[lane + 1];
+  }
+  const uint64_t touched = __ballot(lane < E && o1 > o0);
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+  const uint64_t hit = __ballot(lane < E && o1 > o0 && __popcll(touched & below) == te);
+  if (hit == 0) return false;
+  const int x = __builtin_amdgcn_readfirstlane(__ffsll((unsigned long long)hit) - 1);
+  e = x;
+  row0 = __builtin_amdgcn_readfirstlane(__shfl(o0, x));
+  nrows = __builtin_amdgcn_readfirstlane(__shfl(o1, x) - row0);
+  return true;
+}
+
 // ---------------------------------------------------------------- conversions
 // Eight int8 codes (two dwords, byte 0 first) -> eight bf16 values. Exact: a
 // code has at most 8 significant bits. Compiles to one sign-extending

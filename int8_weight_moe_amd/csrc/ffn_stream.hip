@@ -135,25 +135,10 @@ __global__ __launch_bounds__(stream_block_waves(KS) * kWave) void ffn_stream_ker
   const int kslice = wave % KS;
   const int te = item / gpe;
   const int grp = item - te * gpe;
-  int e = -1, row0 = 0, nrows = 0;
-  {
-    int seen = 0;
-    for (int x = 0; x < E; ++x) {
-      const int o0 = offsets[x], o1 = offsets[x + 1];
-      if (o1 > o0) {
-        if (seen == te) {
-          e = x;
-          row0 = o0;
-          nrows = o1 - o0;
-          break;
-        }
-        ++seen;
-      }
-    }
-  }
+  int e, row0, nrows;
   // With KS > 1 the workgroup is one item: every wave takes this return, the
   // row loop and the barriers below together.
-  if (e < 0) return;
+  if (!find_touched_expert(offsets, E, te, e, row0, nrows)) return;
 
   const int ch_base = grp * 16 * NG;
   // first 1 KiB block of each 16-channel group (tiled layout), this lane's piece
@@ -371,23 +356,8 @@ __global__ __launch_bounds__(W * kWave) void ffn_stream_shared_gu_kernel(
   const int wg_per_e = gpe / W;
   const int te = blockIdx.x / wg_per_e;
   const int grp = (blockIdx.x - te * wg_per_e) * W + wave;
-  int e = -1, row0 = 0, nrows = 0;
-  {
-    int seen = 0;
-    for (int x = 0; x < E; ++x) {
-      const int o0 = offsets[x], o1 = offsets[x + 1];
-      if (o1 > o0) {
-        if (seen == te) {
-          e = x;
-          row0 = o0;
-          nrows = o1 - o0;
-          break;
-        }
-        ++seen;
-      }
-    }
-  }
-  if (e < 0) return;   // the same for every wave of the workgroup
+  int e, row0, nrows;
+  if (!find_touched_expert(offsets, E, te, e, row0, nrows)) return;   // the same for every wave of the workgroup
 
   const int ch_base = grp * 16 * NG;
   const int8_t* wp[NG][NMAT];

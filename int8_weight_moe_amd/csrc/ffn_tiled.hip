@@ -103,22 +103,8 @@ __global__ __launch_bounds__(WM * WN * kWave) void ffn_tiled_kernel(
   const int mt_global = group * GM + in_group % gm;
   const int nt = in_group / gm;
   if (nt >= n_tiles_n) return;
-  int e = -1, row0 = 0, nrows = 0;
-  {
-    int cum = 0;
-    for (int x = 0; x < E; ++x) {
-      const int o0 = offsets[x], o1 = offsets[x + 1];
-      const int mt_e = (o1 - o0 + BM - 1) / BM;
-      if (mt_global < cum + mt_e) {
-        e = x;
-        row0 = o0 + (mt_global - cum) * BM;
-        nrows = min(BM, o1 - row0);
-        break;
-      }
-      cum += mt_e;
-    }
-  }
-  if (e < 0) return;
+  int e, row0, nrows;
+  if (!find_row_tile<BM>(offsets, E, mt_global, e, row0, nrows)) return;
   const int n0 = nt * CH_TILE;
 
   // ---- global source pointers of this thread's pieces
@@ -380,22 +366,8 @@ void ffn_tiled_dma_kernel(
   const int mt_global = group * GM + in_group % gm;
   const int nt = in_group / gm;
   if (nt >= n_tiles_n) return;
-  int e = -1, row0 = 0, nrows = 0;
-  {
-    int cum = 0;
-    for (int x = 0; x < E; ++x) {
-      const int o0 = offsets[x], o1 = offsets[x + 1];
-      const int mt_e = (o1 - o0 + BM - 1) / BM;
-      if (mt_global < cum + mt_e) {
-        e = x;
-        row0 = o0 + (mt_global - cum) * BM;
-        nrows = min(BM, o1 - row0);
-        break;
-      }
-      cum += mt_e;
-    }
-  }
-  if (e < 0) return;
+  int e, row0, nrows;
+  if (!find_row_tile<BM>(offsets, E, mt_global, e, row0, nrows)) return;
   const int n0 = nt * CH_TILE;
 
   // activation sources: instruction j of this wave covers rows 8*(A_INSTR*wave + j) + lane/8;
