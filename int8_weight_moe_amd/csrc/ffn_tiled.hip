@@ -486,6 +486,26 @@ void ffn_tiled_dma_kernel(
   }
 #endif
 
+  // per-lane scales of the channels this lane holds in the result, read before
+  // the main loop so the epilogue waits on no load: gate/up keeps the gate
+  // scales of its HALF channel blocks then the up scales, down its NB blocks
+  // (unscaled encodings and channels past N: 1)
+  float4 scl[NB];
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    scl[j] = make_float4(1.f, 1.f, 1.f, 1.f);
+    if constexpr (WF::kScaled) {
+      if constexpr (kGateUp) {
+        constexpr int HALF = NB / 2;
+        const int ch = n0 + wn * (HALF * 16) + (j % HALF) * 16 + 4 * lg;
+        if (ch < N) scl[j] = load_scale4<kScaleBf16>(j < HALF ? S0 : S1, (long)e * N + ch);
+      } else {
+        const int ch = n0 + wn * TN + j * 16 + 4 * lg;
+        if (ch < N) scl[j] = load_scale4<kScaleBf16>(S0, (long)e * N + ch);
+      }
+    }
+  }
+
   const int nk = Kd >> 6;
   // Every step issues the step STAGES-1 ahead, clamped to the last one: past the
   // end this reloads the last step into a buffer that is no longer read, which
@@ -549,11 +569,7 @@ void ffn_tiled_dma_kernel(
       for (int j = 0; j < HALF; ++j) {
         const int ch = n0 + wn * (HALF * 16) + j * 16 + 4 * lg;
         if (ch >= N) continue;
-        float4 sg = make_float4(1.f, 1.f, 1.f, 1.f), su = sg;
-        if constexpr (WF::kScaled) {
-          sg = load_scale4<kScaleBf16>(S0, (long)e * N + ch);
-          su = load_scale4<kScaleBf16>(S1, (long)e * N + ch);
-        }
+        const float4 sg = scl[j], su = scl[j + HALF];
         const float sgv[4] = {sg.x, sg.y, sg.z, sg.w}, suv[4] = {su.x, su.y, su.z, su.w};
         bf16x4 hv;
 #pragma unroll
@@ -565,8 +581,7 @@ void ffn_tiled_dma_kernel(
       for (int j = 0; j < NB; ++j) {
         const int ch = n0 + wn * TN + j * 16 + 4 * lg;
         if (ch >= N) continue;
-        float4 sd = make_float4(1.f, 1.f, 1.f, 1.f);
-        if constexpr (WF::kScaled) sd = load_scale4<kScaleBf16>(S0, (long)e * N + ch);
+        const float4 sd = scl[j];
         const float4 yv = make_float4(acc[i][j][0] * sd.x, acc[i][j][1] * sd.y, acc[i][j][2] * sd.z, acc[i][j][3] * sd.w);
         *reinterpret_cast<float4*>(static_cast<float*>(out) + orow + ch) = yv;
       }
