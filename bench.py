@@ -155,11 +155,14 @@ def time_stages(layer, x, path, steps, warmup, dense=False):
     the combine are timed."""
     import torch
     from int8_weight_moe_amd import moe_combine, moe_expert_down, moe_expert_gate_up, moe_permute, moe_route
+    from int8_weight_moe_amd.ops import down_workspace_size, make_shape
     ex, K = layer.experts, layer.K
     T = x.shape[0]
     names = ["gate_up", "down", "combine"] if dense else ["route", "permute", "gate_up", "down", "combine"]
     h = torch.empty((T * K, ex.f), dtype=torch.bfloat16, device=x.device)
     rows = torch.empty((T * K, ex.d), dtype=torch.float32, device=x.device)
+    dshape = make_shape(T, ex.d, ex.f, ex.E, K, x.dtype, ex.scale_dtype, path, ex.fmt)
+    dws = torch.empty(max(down_workspace_size(dshape), 256), dtype=torch.uint8, device=x.device)
     if dense:
         ids0, gw0 = moe_route(x, layer.router_w, layer.bias, K)
         layout = (gw0,) + tuple(moe_permute(ids0, ex.E))
@@ -178,7 +181,7 @@ def time_stages(layer, x, path, steps, warmup, dense=False):
             ev[i].record()
         moe_expert_gate_up(x, off, ss, ex, K, path=path, h=h)
         ev[i + 1].record()
-        moe_expert_down(h, off, ex, T, K, act=x.dtype, path=path, y_rows=rows)
+        moe_expert_down(h, off, ex, T, K, act=x.dtype, path=path, y_rows=rows, workspace=dws)
         ev[i + 2].record()
         moe_combine(rows, s2r, gw, x.dtype)
         ev[i + 3].record()

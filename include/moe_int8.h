@@ -103,7 +103,7 @@ typedef struct moe_shape {
 } moe_shape;
 
 /* ABI version of this header (bumped on any signature change). */
-#define MOE_ABI_VERSION 3
+#define MOE_ABI_VERSION 4
 int32_t moe_abi_version(void);
 
 /* Static description of a status code. */
@@ -113,11 +113,20 @@ const char* moe_status_str(moe_status status);
 const char* moe_last_error(void);
 
 /* Workspace, in bytes, that moe_forward needs for this shape (includes the
- * routing buffers, the permutation, h and y_rows). */
+ * routing buffers, the permutation, h, y_rows and the down pass's partial
+ * sums, see moe_down_workspace_size). */
 moe_status moe_workspace_size(const moe_shape* shape, size_t* bytes);
 
-/* Workspace, in bytes, that moe_expert_ffn needs (h: T*K*f bf16, plus padding). */
+/* Workspace, in bytes, that moe_expert_ffn needs: h (T*K*f bf16), then the
+ * down pass's partial sums (moe_down_workspace_size), each padded to 256. */
 moe_status moe_ffn_workspace_size(const moe_shape* shape, size_t* bytes);
+
+/* Workspace, in bytes, that the down pass can use: fp32 partial sums
+ * [planes, T*K, d] for shapes whose weight-streaming down pass splits its
+ * reduction over workgroups (33 to 64 rows per expert on average and too few
+ * output-channel groups to fill the GPU, e.g. a dense MLP at decode); 0 for
+ * every other shape. */
+moe_status moe_down_workspace_size(const moe_shape* shape, size_t* bytes);
 
 /* Router and gate (paper: "Model Architecture", top K of n experts per token).
  *   x           [T, d]  act_dtype
@@ -147,7 +156,7 @@ moe_status moe_permute(const moe_shape* shape, const int32_t* topk_ids,
  *   w_gate, w_up   [E, f, d];  w_down [E, d, f] -- shape->weight_fmt encoding, tiled layout (moe_pack_rows)
  *   s_gate, s_up   [E, f] scale_dtype;  s_down [E, d] scale_dtype (unused for MOE_W_BF16)
  *   y_rows         [T*K, d] fp32 out: row r = output of sorted row r's expert
- *   workspace      >= moe_ffn_workspace_size bytes (holds h)
+ *   workspace      >= moe_ffn_workspace_size bytes (holds h and the down pass's partial sums)
  * Rows past off[E] are left untouched. */
 moe_status moe_expert_ffn(const moe_shape* shape, const void* x,
                           const int32_t* expert_offsets, const int32_t* sorted_slots,
@@ -160,12 +169,20 @@ moe_status moe_expert_ffn(const moe_shape* shape, const void* x,
  * gate/up  h[r] = silu(s_g * (q_g . x_r)) * (s_u * (q_u . x_r))  for every sorted row r,
  *          h [T*K, f] bf16 out (rows past off[E] untouched);
  * down     y_rows[r] = s_d * (q_d . h[r]),  h [T*K, f] bf16 in, y_rows [T*K, d] fp32 out.
- * moe_expert_ffn is moe_expert_gate_up followed by moe_expert_down on the same stream. */
+ *          workspace: NULL, or 16-byte aligned and >= moe_down_workspace_size
+ *          bytes (else MOE_ERR_ALIGN / MOE_ERR_WORKSPACE). With it, a down pass
+ *          that splits its reduction may spread the slices over workgroups
+ *          (partial sums in the workspace, added in slice order by a second
+ *          kernel); without it the slices stay inside one workgroup. y_rows is
+ *          the same bit for bit either way.
+ * moe_expert_ffn is moe_expert_gate_up followed by moe_expert_down on the same
+ * stream, with the part of its workspace after h as the down workspace. */
 moe_status moe_expert_gate_up(const moe_shape* shape, const void* x, const int32_t* expert_offsets,
                               const int32_t* sorted_slots, const void* w_gate, const void* w_up,
                               const void* s_gate, const void* s_up, void* h, hipStream_t stream);
 moe_status moe_expert_down(const moe_shape* shape, const void* h, const int32_t* expert_offsets,
-                           const void* w_down, const void* s_down, float* y_rows, hipStream_t stream);
+                           const void* w_down, const void* s_down, float* y_rows, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream);
 
 /* Weighted combine back to token order: y[t] = sum_k topk_w[t,k] * y_rows[slot_to_row[t*K+k]]
  * (k ascending, fp32, no atomics); a slot with row -1 contributes nothing.

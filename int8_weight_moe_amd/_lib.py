@@ -11,7 +11,7 @@ import os
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libmoe_int8.so")
 
-ABI_VERSION = 3
+ABI_VERSION = 4
 MOE_OK = 0
 STATUS_NAMES = {
     0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_DTYPE", 4: "MOE_ERR_ALIGN",
@@ -25,7 +25,7 @@ MOE_W_INT8, MOE_W_BF16, MOE_W_FP8 = 0, 1, 2
 EXPORTS = (
     "moe_abi_version", "moe_status_str", "moe_last_error", "moe_workspace_size", "moe_ffn_workspace_size",
     "moe_route", "moe_permute", "moe_expert_ffn", "moe_expert_gate_up", "moe_expert_down", "moe_combine", "moe_forward", "moe_quantize_rows",
-    "moe_pack_rows", "moe_mlp_workspace_size", "moe_mlp_forward", "moe_quantize_rows_fp8",
+    "moe_pack_rows", "moe_mlp_workspace_size", "moe_mlp_forward", "moe_quantize_rows_fp8", "moe_down_workspace_size",
 )
 
 
@@ -53,7 +53,8 @@ _SIGS = {
     "moe_permute": (ctypes.c_int32, [_SHAPE, _P, _P, _P, _P, _P]),
     "moe_expert_ffn": (ctypes.c_int32, [_SHAPE, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "moe_expert_gate_up": (ctypes.c_int32, [_SHAPE, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
-    "moe_expert_down": (ctypes.c_int32, [_SHAPE, _P, _P, _P, _P, _P, _P]),
+    "moe_expert_down": (ctypes.c_int32, [_SHAPE, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "moe_down_workspace_size": (ctypes.c_int32, [_SHAPE, ctypes.POINTER(ctypes.c_size_t)]),
     "moe_combine": (ctypes.c_int32, [_SHAPE, _P, _P, _P, _P, _P]),
     "moe_forward": (ctypes.c_int32, [_SHAPE, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "moe_quantize_rows": (ctypes.c_int32, [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_int32, _P, _P, _P]),

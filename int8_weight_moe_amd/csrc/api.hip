@@ -62,8 +62,11 @@ moe_status check_shape(const moe_shape* s) {
   } while (0)
 
 struct WsLayout {
-  size_t ids, w, offsets, sorted, s2r, h, y_rows, total;
+  size_t ids, w, offsets, sorted, s2r, h, y_rows, part, part_bytes, total;
 };
+
+bool use_stream(const moe_shape* s);
+size_t down_ws_bytes(const moe_shape* s);
 
 WsLayout forward_layout(const moe_shape* s) {
   const size_t S = (size_t)s->T * s->K;
@@ -76,11 +79,23 @@ WsLayout forward_layout(const moe_shape* s) {
   L.s2r = o;     o += round_up(S * 4);
   L.h = o;       o += round_up(S * (size_t)s->f * 2);
   L.y_rows = o;  o += round_up(S * (size_t)s->d * 4);
+  // partial sums of a stream down pass split over workgroups (none otherwise)
+  L.part_bytes = down_ws_bytes(s);
+  L.part = o;    o += round_up(L.part_bytes);
   L.total = o;
   return L;
 }
 
-size_t ffn_ws_bytes(const moe_shape* s) { return round_up((size_t)s->T * s->K * (size_t)s->f * 2); }
+// fp32 partial sums of a stream down pass split over workgroups ([planes, S, d]), 0 if it does not split.
+size_t down_ws_bytes(const moe_shape* s) {
+  const long S = (long)s->T * s->K;
+  const int planes = use_stream(s) ? moe::stream_down_planes(S, s->d, s->f, s->E) : 0;
+  return (size_t)planes * (size_t)S * (size_t)s->d * 4;
+}
+
+// moe_expert_ffn: h, then the down pass's partial sums
+size_t ffn_h_bytes(const moe_shape* s) { return round_up((size_t)s->T * s->K * (size_t)s->f * 2); }
+size_t ffn_ws_bytes(const moe_shape* s) { return ffn_h_bytes(s) + round_up(down_ws_bytes(s)); }
 
 bool use_stream(const moe_shape* s) {
   if (s->ffn_path == MOE_PATH_STREAM) return true;
@@ -119,6 +134,7 @@ moe::FfnArgs ffn_args(const moe_shape* s, const void* x, const int32_t* offsets,
   a.s_down = s_down;
   a.h = h;
   a.y_rows = y_rows;
+  a.part = nullptr;
   a.T = s->T;
   a.d = s->d;
   a.f = s->f;
@@ -245,8 +261,9 @@ moe_status moe_expert_ffn(const moe_shape* s, const void* x, const int32_t* expe
   const size_t need = ffn_ws_bytes(s);
   if (workspace_bytes < need)
     return fail(MOE_ERR_WORKSPACE, "workspace_bytes=%zu < required %zu", workspace_bytes, need);
-  const moe::FfnArgs a = ffn_args(s, x, expert_offsets, sorted_slots, w_gate, w_up, w_down, s_gate, s_up, s_down,
-                                  y_rows, static_cast<__bf16*>(workspace));
+  moe::FfnArgs a = ffn_args(s, x, expert_offsets, sorted_slots, w_gate, w_up, w_down, s_gate, s_up, s_down, y_rows,
+                            static_cast<__bf16*>(workspace));
+  if (down_ws_bytes(s)) a.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + ffn_h_bytes(s));
   st = run_gate_up(s, a, stream);
   if (st != MOE_OK) return st;
   return run_down(s, a, stream);
@@ -274,7 +291,8 @@ moe_status moe_expert_gate_up(const moe_shape* s, const void* x, const int32_t* 
 }
 
 moe_status moe_expert_down(const moe_shape* s, const void* h, const int32_t* expert_offsets, const void* w_down,
-                           const void* s_down, float* y_rows, hipStream_t stream) {
+                           const void* s_down, float* y_rows, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
   moe_status st = check_shape(s);
   if (st != MOE_OK) return st;
   st = check_ffn(s);
@@ -285,9 +303,24 @@ moe_status moe_expert_down(const moe_shape* s, const void* h, const int32_t* exp
   REQUIRE_PTR(w_down);
   REQUIRE_SCALE(s, s_down);
   REQUIRE_PTR(y_rows);
-  const moe::FfnArgs a = ffn_args(s, nullptr, expert_offsets, nullptr, nullptr, nullptr, w_down, nullptr, nullptr,
-                                  s_down, y_rows, static_cast<__bf16*>(const_cast<void*>(h)));
+  const size_t need = down_ws_bytes(s);
+  if (workspace) {
+    if (!aligned16(workspace)) return fail(MOE_ERR_ALIGN, "workspace is not 16-byte aligned");
+    if (workspace_bytes < need)
+      return fail(MOE_ERR_WORKSPACE, "workspace_bytes=%zu < required %zu", workspace_bytes, need);
+  }
+  moe::FfnArgs a = ffn_args(s, nullptr, expert_offsets, nullptr, nullptr, nullptr, w_down, nullptr, nullptr, s_down,
+                            y_rows, static_cast<__bf16*>(const_cast<void*>(h)));
+  if (workspace && need) a.part = static_cast<float*>(workspace);
   return run_down(s, a, stream);
+}
+
+moe_status moe_down_workspace_size(const moe_shape* shape, size_t* bytes) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (!bytes) return fail(MOE_ERR_NULL, "bytes is NULL");
+  *bytes = down_ws_bytes(shape);
+  return MOE_OK;
 }
 
 moe_status moe_combine(const moe_shape* s, const float* y_rows, const int32_t* slot_to_row,
@@ -345,7 +378,8 @@ moe_status moe_forward(const moe_shape* s, const void* x, const void* router_w, 
   if (e != hipSuccess) return hip_fail(e, "router launch");
   e = moe::launch_permute(ids, s->T * s->K, s->E, offsets, sorted, s2r, stream);
   if (e != hipSuccess) return hip_fail(e, "permute launch");
-  const moe::FfnArgs a = ffn_args(s, x, offsets, sorted, w_gate, w_up, w_down, s_gate, s_up, s_down, y_rows, h);
+  moe::FfnArgs a = ffn_args(s, x, offsets, sorted, w_gate, w_up, w_down, s_gate, s_up, s_down, y_rows, h);
+  if (L.part_bytes) a.part = reinterpret_cast<float*>(ws + L.part);
   st = run_gate_up(s, a, stream);
   if (st != MOE_OK) return st;
   st = run_down(s, a, stream);
@@ -394,7 +428,8 @@ moe_status moe_mlp_forward(const moe_shape* s, const void* x, const void* w_gate
   float* y_rows = reinterpret_cast<float*>(ws + L.y_rows);
   hipError_t e = moe::launch_dense_init(s->T, offsets, sorted, s2r, wts, stream);
   if (e != hipSuccess) return hip_fail(e, "dense init launch");
-  const moe::FfnArgs a = ffn_args(s, x, offsets, sorted, w_gate, w_up, w_down, s_gate, s_up, s_down, y_rows, h);
+  moe::FfnArgs a = ffn_args(s, x, offsets, sorted, w_gate, w_up, w_down, s_gate, s_up, s_down, y_rows, h);
+  if (L.part_bytes) a.part = reinterpret_cast<float*>(ws + L.part);
   st = run_gate_up(s, a, stream);
   if (st != MOE_OK) return st;
   st = run_down(s, a, stream);

@@ -91,6 +91,19 @@ namespace {
 #ifndef MOE_STREAM_SHARED_MIN_WGS
 #define MOE_STREAM_SHARED_MIN_WGS 256
 #endif
+// the 64-row down pass with a reduction split: with a workspace for the
+// slices' partial sums (1), workgroups of SHARED_DN_WAVES waves share each
+// slice's activations through LDS and a second kernel adds the slices;
+// without one (0, or no workspace) the slices stay inside one workgroup
+#ifndef MOE_STREAM_SHARED_DN
+#define MOE_STREAM_SHARED_DN 1
+#endif
+#ifndef MOE_STREAM_SHARED_DN_WAVES
+#define MOE_STREAM_SHARED_DN_WAVES 4
+#endif
+#ifndef MOE_STREAM_P_SHARED_DN
+#define MOE_STREAM_P_SHARED_DN 6
+#endif
 constexpr int kStreamWaves = MOE_STREAM_WAVES;
 
 constexpr int ring_gcd(int a, int b) { return b == 0 ? a : ring_gcd(b, a % b); }
@@ -484,6 +497,181 @@ __global__ __launch_bounds__(W * kWave) void ffn_stream_shared_gu_kernel(
   }
 }
 
+// Down pass of the 64-row variant with the reduction split over workgroups.
+// Workgroup (channel block, slice ks) holds W consecutive items of one expert
+// (no split inside the workgroup) and streams reduction slice ks, the same
+// slice boundaries as the in-workgroup split of ffn_stream_kernel; per
+// 64-wide step its waves copy the 64-row tile of h (8 KiB) once into a P-deep
+// LDS ring with direct-to-LDS loads, and each wave streams its own weight
+// blocks into a P-deep register ring. The slice's fp32 sums (unscaled) go to
+// plane ks of `part` ([KS, S, N]); split_down_reduce adds the planes in
+// ascending slice order and applies the scale. Every MFMA, the sum order and
+// the scaling are those of ffn_stream_kernel with the same split, so y_rows
+// is the same bit for bit.
+template <int F, int NG, int W, int P>
+__global__ __launch_bounds__(W * kWave) void ffn_stream_shared_dn_kernel(
+    const __bf16* __restrict__ H, const int8_t* __restrict__ W0, const int32_t* __restrict__ offsets, int E, int N,
+    int Kd, int S, int KS, float* __restrict__ part) {
+  constexpr int RB = 4;
+  constexpr int ROWS = 16 * RB;
+  using WF = WFormat<F>;
+  constexpr int PPS = WF::kPieces;
+  constexpr int STAGE = ROWS * 128;
+  constexpr int A_TOT = STAGE / 1024;
+  constexpr int A_MAX = (A_TOT + W - 1) / W;
+  constexpr int A_MIN = A_TOT / W;
+  constexpr int NWI = NG * PPS;              // weight loads per wave and step
+  static_assert((P - 2) * (NWI + A_MAX) <= 63, "the vmcnt field holds at most 63");
+  __shared__ __attribute__((aligned(1024))) uint8_t act[P][STAGE];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int li = lane & 15;
+  const int lg = lane >> 4;
+
+  // ---- workgroup -> (slice, expert among the touched ones, W consecutive items)
+  const int gpe = N / (16 * NG);
+  const int wg_per_e = gpe / W;
+  const int ks = blockIdx.x % KS;
+  const int rest = blockIdx.x / KS;
+  const int te = rest / wg_per_e;
+  const int grp = (rest - te * wg_per_e) * W + wave;
+  int e, row0, nrows;
+  if (!find_touched_expert(offsets, E, te, e, row0, nrows)) return;   // the same for the whole workgroup
+
+  const int ch_base = grp * 16 * NG;
+  const int8_t* wp[NG];
+#pragma unroll
+  for (int ng = 0; ng < NG; ++ng) {
+    const long group = ((long)e * N + ch_base + ng * 16) >> 4;
+    wp[ng] = W0 + group * (long)(Kd >> 6) * (1024 * PPS) + 16 * lane;
+  }
+  const int nsteps_all = Kd >> 6;
+  const int s_base = ks * nsteps_all / KS;
+  const int nsteps = (ks + 1) * nsteps_all / KS - s_base;
+  float* plane = part + (long)ks * S * N;
+
+  for (int p0 = 0; p0 < nrows; p0 += ROWS) {
+    const int prow = min(ROWS, nrows - p0);
+    const int nrb = (prow + 15) >> 4;
+    // this wave's activation DMAs: tile instruction c = wave + W*j covers rows
+    // 8c..8c+7; lane l writes row 8c + l/8, chunk slot l%8, fetched from the
+    // logical chunk slot ^ (row % 8); rows past the pass re-read row 0
+    uint32_t a_off[A_MAX];
+#pragma unroll
+    for (int j = 0; j < A_MAX; ++j) {
+      const int c = min(wave + W * j, A_TOT - 1);
+      const int r = 8 * c + (lane >> 3);
+      const int rr = (r < prow) ? r : 0;
+      const int chunk = (lane & 7) ^ (r & 7);
+      a_off[j] = ((uint32_t)(row0 + p0 + rr) * (uint32_t)Kd + (uint32_t)(s_base * 64 + chunk * 8)) * 2u;
+    }
+
+    f32x4 acc[RB][NG];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int ng = 0; ng < NG; ++ng) acc[rb][ng] = f32x4{0.f, 0.f, 0.f, 0.f};
+    uint4 bw[P][NG][PPS];
+
+    auto issue = [&](int t, int st) {
+#pragma unroll
+      for (int ng = 0; ng < NG; ++ng)
+#pragma unroll
+        for (int q = 0; q < PPS; ++q) bw[st][ng][q] = load_nt16(wp[ng] + ((long)(s_base + t) * PPS + q) * 1024);
+#pragma unroll
+      for (int j = 0; j < A_MAX; ++j)
+        if (wave + W * j < A_TOT)
+          dma16(H, a_off[j] + (uint32_t)t * 128u, lds_addr(&act[st][0]) + (wave + W * j) * 1024);
+    };
+    auto compute = [&](int st) {
+      bf16x8 xf[RB][2];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        if (rb < nrb) {
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2) {
+            const int row = rb * 16 + li;
+            const int chunk = ((WF::kActLane * lg + WF::kActSecond * h2) >> 3) ^ (row & 7);
+            xf[rb][h2] = *reinterpret_cast<const bf16x8*>(&act[st][row * 128 + chunk * 16]);
+          }
+        }
+      }
+#pragma unroll
+      for (int ng = 0; ng < NG; ++ng) {
+        bf16x8 w_lo, w_hi;
+        WF::operands(bw[st][ng], w_lo, w_hi);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          if (rb < nrb) {
+            acc[rb][ng] = mfma_bf16(w_lo, xf[rb][0], acc[rb][ng]);
+            acc[rb][ng] = mfma_bf16(w_hi, xf[rb][1], acc[rb][ng]);
+          }
+        }
+      }
+    };
+
+#pragma unroll
+    for (int t = 0; t < P - 1; ++t) issue(min(t, nsteps - 1), t);
+    for (int s0 = 0; s0 < nsteps; s0 += P) {
+#pragma unroll
+      for (int j = 0; j < P; ++j) {
+        if (s0 + j < nsteps) {   // the same for every wave
+          __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0((P - 2) * (NWI + A_MIN)));
+          __builtin_amdgcn_s_barrier();
+          issue(min(s0 + j + P - 1, nsteps - 1), (j + P - 1) % P);
+          compute(j);
+        }
+      }
+    }
+    // no load may still be writing the ring when it is reused or the waves exit
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+    __builtin_amdgcn_s_barrier();
+
+    // ---- this slice's sums: lane holds channels ch_base + ng*16 + 4*lg + q, row p0 + rb*16 + li
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const int r = p0 + rb * 16 + li;
+      if (rb < nrb && r < nrows) {
+        const long orow = (long)(row0 + r) * N;
+#pragma unroll
+        for (int ng = 0; ng < NG; ++ng)
+          *reinterpret_cast<f32x4*>(plane + orow + ch_base + ng * 16 + 4 * lg) = acc[rb][ng];
+      }
+    }
+  }
+}
+
+// y_rows[r, c] = ((part[0] + part[1]) + ...) + part[KS-1], times the channel
+// scale of row r's expert (unscaled encodings: 1); rows of no expert are left
+// as they are. One workgroup per (row, 1024 channels), four channels a thread.
+template <bool kScaleBf16, bool kScaled>
+__global__ __launch_bounds__(256) void split_down_reduce_kernel(const float* __restrict__ part, int KS, int S, int N,
+                                                                const int32_t* __restrict__ offsets, int E,
+                                                                const void* __restrict__ S0,
+                                                                float* __restrict__ y_rows) {
+  const int r = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  int o0 = 0, o1 = 0;
+  if (lane < E) {
+    o0 = offsets[lane];
+    o1 = offsets[lane + 1];
+  }
+  const uint64_t hit = __ballot(lane < E && r >= o0 && r < o1);
+  if (hit == 0) return;   // the same for the whole workgroup
+  const int e = __ffsll((unsigned long long)hit) - 1;
+  const int c = (blockIdx.x * 256 + threadIdx.x) * 4;
+  if (c >= N) return;
+  const long o = (long)r * N + c;
+  f32x4 v = *reinterpret_cast<const f32x4*>(part + o);
+  for (int j = 1; j < KS; ++j) v += *reinterpret_cast<const f32x4*>(part + (long)j * S * N + o);
+  if constexpr (kScaled) {
+    const float4 sc = load_scale4<kScaleBf16>(S0, (long)e * N + c);
+    v = f32x4{v[0] * sc.x, v[1] * sc.y, v[2] * sc.z, v[3] * sc.w};
+  }
+  *reinterpret_cast<f32x4*>(y_rows + o) = v;
+}
+
 template <bool kGateUp, typename Act, bool kScaleBf16, int F, int RB, int KS>
 hipError_t launch_stream_pass_ks(const FfnArgs& a, long items, hipStream_t stream) {
   constexpr int NG = kGateUp ? (RB >= 4 ? MOE_STREAM_NG_GU_WIDE : MOE_STREAM_NG_GU)
@@ -549,17 +737,61 @@ hipError_t launch_stream_shared_gu(const FfnArgs& a, hipStream_t stream) {
   }
 }
 
+// Partial-sum planes the 64-row down pass with a reduction split across
+// workgroups needs ([planes, S, d] fp32), or 0 when it is not taken: fewer
+// than 33 rows per expert on average, no split, a slice without a step, h
+// offsets past 32 bits, or channel groups of an expert that do not fill
+// whole workgroups.
+int shared_down_planes(long S, int d, int f, int E) {
+  constexpr int NG = MOE_STREAM_NG_DN_WIDE, W = MOE_STREAM_SHARED_DN_WAVES;
+  if (!MOE_STREAM_SHARED_DN || S <= 32L * E) return 0;
+  if ((uint64_t)S * f * 2 >= (1ull << 32)) return 0;
+  const int gpe = d / (16 * NG);
+  if (gpe % W) return 0;
+  const int ks = choose_split((long)E * gpe, 4);
+  if (ks <= 1 || (f >> 6) < ks) return 0;
+  return ks;
+}
+
+template <int F>
+hipError_t launch_stream_shared_dn(const FfnArgs& a, int KS, hipStream_t stream) {
+  constexpr int NG = MOE_STREAM_NG_DN_WIDE, W = MOE_STREAM_SHARED_DN_WAVES;
+  const int gpe = a.d / (16 * NG);
+  const dim3 grid((unsigned)((long)a.E * (gpe / W) * KS));
+  hipLaunchKernelGGL((ffn_stream_shared_dn_kernel<F, NG, W, MOE_STREAM_P_SHARED_DN>), grid, dim3(W * kWave), 0,
+                     stream, static_cast<const __bf16*>(a.h), a.w_down, a.offsets, a.E, a.d, a.f, a.S, KS, a.part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 rgrid((unsigned)((a.d + 1023) / 1024), (unsigned)a.S);
+  if (!WFormat<F>::kScaled) {
+    hipLaunchKernelGGL((split_down_reduce_kernel<true, false>), rgrid, dim3(256), 0, stream, a.part, KS, a.S, a.d,
+                       a.offsets, a.E, a.s_down, a.y_rows);
+  } else if (a.scale_bf16) {
+    hipLaunchKernelGGL((split_down_reduce_kernel<true, true>), rgrid, dim3(256), 0, stream, a.part, KS, a.S, a.d,
+                       a.offsets, a.E, a.s_down, a.y_rows);
+  } else {
+    hipLaunchKernelGGL((split_down_reduce_kernel<false, true>), rgrid, dim3(256), 0, stream, a.part, KS, a.S, a.d,
+                       a.offsets, a.E, a.s_down, a.y_rows);
+  }
+  return hipGetLastError();
+}
+
 // Rows per pass: 16*RB. More than 32 rows per expert on average (a dense MLP
 // layer, or a hot expert at decode) takes the 64-row variant so the weights
 // are streamed once; otherwise the 32-row variant keeps more waves resident.
 // The 64-row gate/up pass with bf16 activations shares them through LDS when
-// their byte offsets fit 32 bits.
+// their byte offsets fit 32 bits; so does the 64-row down pass with a
+// reduction split when the caller gives it the partial-sum planes.
 template <bool kGateUp, typename Act, bool kScaleBf16, int F>
 hipError_t launch_stream_pass(const FfnArgs& a, hipStream_t stream) {
   if ((long)a.S > 32L * a.E) {
     if constexpr (kGateUp && sizeof(Act) == 2) {
       if (MOE_STREAM_SHARED_GU && (uint64_t)a.T * a.d * 2 < (1ull << 32))
         return launch_stream_shared_gu<kScaleBf16, F>(a, stream);
+    }
+    if constexpr (!kGateUp) {
+      const int planes = shared_down_planes(a.S, a.d, a.f, a.E);
+      if (a.part && planes > 0) return launch_stream_shared_dn<F>(a, planes, stream);
     }
     return launch_stream_pass_rb<kGateUp, Act, kScaleBf16, F, 4>(a, stream);
   }
@@ -591,6 +823,8 @@ hipError_t dispatch_stream(const FfnArgs& a, hipStream_t stream) {
 }
 
 }  // namespace
+
+int stream_down_planes(long S, int d, int f, int E) { return shared_down_planes(S, d, f, E); }
 
 hipError_t launch_stream_gate_up(const FfnArgs& a, hipStream_t stream) { return dispatch_stream<true>(a, stream); }
 hipError_t launch_stream_down(const FfnArgs& a, hipStream_t stream) { return dispatch_stream<false>(a, stream); }

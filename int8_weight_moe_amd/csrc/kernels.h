@@ -30,6 +30,7 @@ struct FfnArgs {
   const void* s_down;         // [E, d]
   __bf16* h;                  // [S, f] scratch
   float* y_rows;              // [S, d] out
+  float* part;                // [planes, S, d] scratch of a down pass split over workgroups, or null
   int T, d, f, E, K, S;
 };
 
@@ -37,6 +38,10 @@ struct FfnArgs {
 // (x -> h) and down pass (h -> y_rows).
 hipError_t launch_stream_gate_up(const FfnArgs& a, hipStream_t stream);
 hipError_t launch_stream_down(const FfnArgs& a, hipStream_t stream);
+// Partial-sum planes ([planes, S, d] fp32, in FfnArgs::part) with which the
+// stream down pass splits its reduction over workgroups; 0: it does not. With
+// part null the pass keeps the split inside one workgroup, with the same result.
+int stream_down_planes(long S, int d, int f, int E);
 // Tiled MFMA schedule for many rows per expert (prefill). bf16 and fp8
 // weights need bf16 activations and dma_offsets_fit(T, S, d, f, bytes per
 // weight); int8 weights take any shape.

@@ -157,16 +157,32 @@ def moe_expert_gate_up(x: torch.Tensor, expert_offsets: torch.Tensor, sorted_slo
     return h
 
 
+def down_workspace_size(shape: MoeShape) -> int:
+    lib = _lib_handle()
+    n = ctypes.c_size_t(0)
+    _lib.check(lib.moe_down_workspace_size(ctypes.byref(shape), ctypes.byref(n)))
+    return n.value
+
+
 def moe_expert_down(h: torch.Tensor, expert_offsets: torch.Tensor, experts: Int8Experts, T: int, K: int,
                     act: torch.dtype = torch.bfloat16, path: int = MOE_PATH_AUTO,
-                    y_rows: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Down pass: y_rows [T*K, d] fp32 from h [T*K, f] bf16."""
+                    y_rows: Optional[torch.Tensor] = None, split_workspace: bool = True,
+                    workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Down pass: y_rows [T*K, d] fp32 from h [T*K, f] bf16. With split_workspace the
+    call gets the partial-sum workspace it can use (`workspace` if given, else a new
+    one; none for most shapes); without it a split reduction stays inside one
+    workgroup (same result, bit for bit)."""
     lib = _lib_handle()
     shape = make_shape(T, experts.d, experts.f, experts.E, K, act, experts.scale_dtype, path, experts.fmt)
     if y_rows is None:
         y_rows = torch.empty((T * K, experts.d), dtype=torch.float32, device=h.device)
+    ws = None
+    need = down_workspace_size(shape) if split_workspace else 0
+    if need:
+        ws = workspace if workspace is not None else torch.empty(need, dtype=torch.uint8, device=h.device)
     _lib.check(lib.moe_expert_down(ctypes.byref(shape), _ptr(h), _ptr(expert_offsets), _ptr(experts.q_down),
-                                   _ptr(experts.s_down), _ptr(y_rows), _stream()))
+                                   _ptr(experts.s_down), _ptr(y_rows), _ptr(ws),
+                                   ctypes.c_size_t(ws.numel() if ws is not None else 0), _stream()))
     return y_rows
 
 

@@ -111,6 +111,47 @@ def test_workspace_checks(lib):
     assert st == 5
 
 
+def test_workspace_holds_split_down_planes(lib):
+    """A stream down pass whose reduction splits 8 ways over workgroups gets 8
+    fp32 partial-sum planes [8, S, d] after y_rows; other shapes get none."""
+    r = lambda v: (v + 255) // 256 * 256
+
+    def sizes(T, d, f, E, K, path):
+        s = _shape(T=T, d=d, f=f, E=E, K=K, ffn_path=path)
+        n = ctypes.c_size_t(0)
+        assert lib.moe_workspace_size(ctypes.byref(s), ctypes.byref(n)) == 0
+        S = T * K
+        base = 4 * r(S * 4) + r((E + 1) * 4) + r(S * f * 2) + r(S * d * 4)
+        return n.value, base, S
+
+    # dense MLP at decode (64 rows on one expert, 256 items of 32 channels: 8-way split)
+    n, base, S = sizes(64, 8192, 24576, 1, 1, 0)
+    assert n == base + r(8 * S * 8192 * 4)
+    m = ctypes.c_size_t(0)
+    s = _shape(T=64, d=8192, f=24576, E=1, K=1)
+    assert lib.moe_mlp_workspace_size(ctypes.byref(s), ctypes.byref(m)) == 0 and m.value == n
+    # 37 rows per expert on the stream schedule, 8 reduction steps: split
+    n, base, S = sizes(300, 256, 512, 16, 2, 1)
+    assert n == base + r(8 * S * 256 * 4)
+    # the down pass alone: the planes, or an error for a short or misaligned workspace
+    s = _shape(T=300, d=256, f=512, E=16, K=2, ffn_path=1)
+    dn = ctypes.c_size_t(0)
+    assert lib.moe_down_workspace_size(ctypes.byref(s), ctypes.byref(dn)) == 0 and dn.value == 8 * S * 256 * 4
+    assert lib.moe_expert_down(ctypes.byref(s), A, A, A, A, A, A, ctypes.c_size_t(dn.value - 1), None) == 5
+    assert lib.moe_expert_down(ctypes.byref(s), A, A, A, A, A, MIS, ctypes.c_size_t(dn.value), None) == 4
+    f = ctypes.c_size_t(0)
+    assert lib.moe_ffn_workspace_size(ctypes.byref(s), ctypes.byref(f)) == 0
+    assert f.value == r(S * 512 * 2) + r(dn.value)
+    # the same with 6 reduction steps (fewer than the split): none
+    n, base, _ = sizes(300, 256, 384, 16, 2, 1)
+    assert n == base
+    # at most 32 rows per expert (the 32-row variant), or the tiled schedule: none
+    n, base, _ = sizes(256, 256, 512, 16, 2, 1)
+    assert n == base
+    n, base, _ = sizes(300, 256, 512, 16, 2, 2)
+    assert n == base
+
+
 def test_empty_input_enqueues_nothing(lib):
     s = _shape(T=0)
     need = ctypes.c_size_t(0)
@@ -175,4 +216,4 @@ def test_weight_format_rules(lib):
         assert lib.moe_forward(ctypes.byref(s), A, A, None, A, A, A, A, A, A, A, None, None, A,
                                ctypes.c_size_t(1 << 30), None) == 6
         assert b"bf16 activations" in lib.moe_last_error()
-        assert lib.moe_expert_down(ctypes.byref(s), A, A, A, A, A, None) == 6
+        assert lib.moe_expert_down(ctypes.byref(s), A, A, A, A, A, None, 0, None) == 6
