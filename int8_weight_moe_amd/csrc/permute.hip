@@ -6,12 +6,13 @@
 // the MoE layer is I/O-bound).
 //
 // One workgroup of 16 waves. Wave w owns a contiguous range of slots, walked
-// in 64-slot chunks. Pass 1 counts, per chunk and expert, the lanes whose id
-// matches (a ballot and a popcount), accumulated by the lane that owns that
-// expert. The 16 x E counts are scanned in a fixed order (expert-major, then
-// wave) by the whole workgroup, one count per thread. Pass 2 walks the same
-// chunks again and gives each slot its position: the expert's running base
-// plus the number of matching lanes below it in the ballot. Slots therefore keep ascending order inside an expert, and
+// in 64-slot chunks (the ids of 8 chunks loaded together). Pass 1 counts, per
+// chunk and expert, the lanes whose id matches (a ballot and a popcount),
+// accumulated by the lane that owns that expert. The 16 x E counts are scanned
+// in a fixed order (expert-major, then wave) by the whole workgroup, one count
+// per thread. Pass 2 walks the same chunks again and gives each slot its
+// position: the expert's running base plus the number of matching lanes below
+// it in the ballot. Slots therefore keep ascending order inside an expert, and
 // the result is bit-exact and independent of scheduling.
 #include "device_common.h"
 #include "kernels.h"
@@ -22,6 +23,7 @@ namespace {
 
 constexpr int kPermWaves = 16;
 constexpr int kMaxExperts = 64;
+constexpr int kBatch = 8;   // 64-slot chunks whose ids a wave loads at once
 
 __global__ __launch_bounds__(kPermWaves * kWave) void permute_kernel(const int32_t* __restrict__ ids, int S, int E,
                                                                      int32_t* __restrict__ offsets,
@@ -41,12 +43,19 @@ __global__ __launch_bounds__(kPermWaves * kWave) void permute_kernel(const int32
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 
   int my_count = 0;  // lane e counts expert e
-  for (int s0 = s_begin; s0 < s_end; s0 += 64) {
-    const int s = s0 + lane;
-    const int id = (s < s_end) ? ids[s] : -1;
-    for (int e = 0; e < E; ++e) {
-      const uint64_t m = __ballot(id == e);
-      if (lane == e) my_count += __popcll(m);
+  for (int s0 = s_begin; s0 < s_end; s0 += 64 * kBatch) {
+    int idv[kBatch];   // the batch's ids are loaded together: one memory latency per batch
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+      const int s = s0 + 64 * b + lane;
+      idv[b] = (s < s_end) ? ids[s] : -1;
+    }
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+      for (int e = 0; e < E; ++e) {
+        const uint64_t m = __ballot(idv[b] == e);
+        if (lane == e) my_count += __popcll(m);
+      }
     }
   }
   cnt[wave][lane] = my_count;
@@ -82,20 +91,28 @@ __global__ __launch_bounds__(kPermWaves * kWave) void permute_kernel(const int32
   __syncthreads();
 
   int my_base = (lane < E) ? base[wave][lane] : 0;
-  for (int s0 = s_begin; s0 < s_end; s0 += 64) {
-    const int s = s0 + lane;
-    const bool in = s < s_end;
-    const int id = in ? ids[s] : -1;
-    int pos = -1;
-    for (int e = 0; e < E; ++e) {
-      const uint64_t m = __ballot(id == e);
-      const int b = __shfl(my_base, e);
-      if (id == e) pos = b + __popcll(m & below);
-      if (lane == e) my_base += __popcll(m);
+  for (int s0 = s_begin; s0 < s_end; s0 += 64 * kBatch) {
+    int idv[kBatch];
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+      const int s = s0 + 64 * b + lane;
+      idv[b] = (s < s_end) ? ids[s] : -1;
     }
-    if (in) {
-      slot_to_row[s] = pos;
-      if (pos >= 0) sorted_slots[pos] = s;
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+      const int s = s0 + 64 * b + lane;
+      const int id = idv[b];
+      int pos = -1;
+      for (int e = 0; e < E; ++e) {
+        const uint64_t m = __ballot(id == e);
+        const int bs = __builtin_amdgcn_readlane(my_base, e);   // e is uniform: a scalar read of lane e
+        if (id == e) pos = bs + __popcll(m & below);
+        if (lane == e) my_base += __popcll(m);
+      }
+      if (s < s_end) {
+        slot_to_row[s] = pos;
+        if (pos >= 0) sorted_slots[pos] = s;
+      }
     }
   }
   // rows past the placed slots (only when some id was out of range)

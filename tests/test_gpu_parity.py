@@ -110,6 +110,7 @@ def test_route_exact_ties_go_to_lower_index():
 @pytest.mark.parametrize("T,K,E,kind", [
     (1, 2, 16, "rand"), (64, 2, 16, "rand"), (1000, 2, 16, "hot"), (4096, 2, 16, "one"),
     (333, 3, 5, "rand"), (16384, 2, 16, "hot"), (70, 1, 64, "rand"), (7, 8, 8, "perm"),
+    (20001, 2, 16, "rand"),   # 40002 slots: several 8-chunk batches per wave and a ragged last one
 ])
 def test_permute_bit_exact(T, K, E, kind):
     rng = np.random.default_rng(T + K + E)
