@@ -24,6 +24,13 @@
 // slices streamed by the KS waves of one workgroup; the slices' fp32 partial
 // sums are added through LDS in ascending slice order before the epilogue, so
 // the result does not depend on scheduling and costs no extra HBM traffic.
+// With more than 32 rows per expert every wave would re-read its rows'
+// activations from L2 at each step, so two variants share them through LDS
+// among the waves of a workgroup that work on neighbouring channel groups:
+// the gate/up pass (ffn_stream_shared_gu_kernel), and the down pass with a
+// split reduction when the caller provides a workspace for the slices' sums
+// (ffn_stream_shared_dn_kernel + split_down_reduce_kernel, bitwise the same
+// result as the in-workgroup split).
 // Gate/up pass: g and u accumulate side by side; the epilogue applies the
 // per-channel scales and SwiGLU and stores h (bf16). Down pass: the epilogue
 // applies the down scale and stores y_rows (fp32).

@@ -461,30 +461,15 @@ void ffn_tiled_dma_kernel(
     }                                                                                               \
   }
 
-// The MFMAs of one sub-step. Variant 0: all weight fragments converted, then
-// the i-j MFMA nest. Variant 1: fragment j converted right before its MFMAs
-// (j outer). Variant 2: as 1, with scheduling groups pinning the interleave.
-#ifndef MOE_DMA_SCHED
-#define MOE_DMA_SCHED 0
-#endif
-#if MOE_DMA_SCHED == 0
+// The MFMAs of one sub-step: every weight fragment converted, then the i-j
+// MFMA nest (the compiler interleaves the two; pinning the interleave with
+// scheduling groups, or converting fragment j right before its MFMAs,
+// measured slower).
 #define MOE_DMA_MMA(MBV)                                                                            \
   _Pragma("unroll") for (int j = 0; j < NB; ++j) wf[j] = WF::operand(wq[j], ks);                    \
   _Pragma("unroll") for (int i = 0; i < MB; ++i)                                                    \
     if (i < (MBV))                                                                                  \
       _Pragma("unroll") for (int j = 0; j < NB; ++j) acc[i][j] = mfma_bf16(wf[j], xf[i], acc[i][j]);
-#else
-#define MOE_DMA_MMA(MBV)                                                                            \
-  _Pragma("unroll") for (int j = 0; j < NB; ++j) {                                                  \
-    wf[j] = WF::operand(wq[j], ks);                                                                 \
-    _Pragma("unroll") for (int i = 0; i < MB; ++i)                                                  \
-      if (i < (MBV)) acc[i][j] = mfma_bf16(wf[j], xf[i], acc[i][j]);                                \
-    if (MOE_DMA_SCHED == 2) {                                                                       \
-      __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);                                           \
-      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);                                            \
-    }                                                                                               \
-  }
-#endif
 
   // per-lane scales of the channels this lane holds in the result, read before
   // the main loop so the epilogue waits on no load: gate/up keeps the gate
