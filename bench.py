@@ -36,7 +36,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 
 # decode workload -> the prefill workload with the same weights
 SIBLING = {"mini-decode": "mini-prefill", "large-decode": "large-prefill-skewed",
-           "large-mlp-decode": "large-mlp-prefill"}
+           "large-mlp-decode": "large-mlp-prefill", "large-decode-tp8": "large-prefill-skewed-tp8"}
 
 
 def parse():

@@ -1,5 +1,8 @@
 """GPU parity at the full workload sizes, in the launch configuration bench.py times.
 
+Also run: one GPU's share of the Large layer under 8-way tensor parallelism
+(f = 3072, workloads.SHARD_WORKLOADS).
+
 Weights are drawn on the GPU by workloads.py and quantized by the library's
 moe_quantize_rows; the layer runs through MoeLayer.forward (moe_forward, auto
 schedule). What the oracle can afford at these sizes:
@@ -33,7 +36,8 @@ pytestmark = pytest.mark.gpu
 
 # experts the oracle re-quantizes and evaluates per workload (CPU time bound)
 ROWS_PER_EXPERT = 256
-EXPERT_BUDGET = {"tiny": 16, "mini-decode": 3, "mini-prefill": 2, "large-decode": 2, "large-prefill-skewed": 2}
+EXPERT_BUDGET = {"tiny": 16, "mini-decode": 3, "mini-prefill": 2, "large-decode": 2, "large-prefill-skewed": 2,
+                 "large-decode-tp8": 3, "large-prefill-skewed-tp8": 2}
 
 
 def _say(msg):
@@ -60,9 +64,9 @@ def _pick_experts(ids: np.ndarray, flags: np.ndarray, budget: int):
     return sorted(chosen)
 
 
-@pytest.fixture(scope="module", params=list(workloads.WORKLOADS))
+@pytest.fixture(scope="module", params=list(workloads.WORKLOADS) + list(workloads.SHARD_WORKLOADS))
 def run(request):
-    w = workloads.WORKLOADS[request.param]
+    w = workloads.ALL_WORKLOADS[request.param]
     dev = torch.device("cuda:0")
     _say(f"{w.name}: drawing inputs T={w.T} d={w.d} f={w.f}")
     src = workloads.draw_expert_weights(w, dev)

@@ -70,7 +70,16 @@ WORKLOADS = {w.name: w for w in (TINY, MINI_DECODE, MINI_PREFILL, LARGE_DECODE, 
 LARGE_MLP_DECODE = Workload("large-mlp-decode", T=64, d=8192, f=24576, E=1, K=1)
 LARGE_MLP_PREFILL = Workload("large-mlp-prefill", T=8192, d=8192, f=24576, E=1, K=1)
 DENSE_WORKLOADS = {w.name: w for w in (LARGE_MLP_DECODE, LARGE_MLP_PREFILL)}
-ALL_WORKLOADS = {**WORKLOADS, **DENSE_WORKLOADS}
+
+# One GPU's share of the Large layer under 8-way tensor parallelism over the
+# expert width: every GPU routes all tokens and holds f/8 = 3072 channels of
+# every expert's gate and up and the matching columns of down, so it runs the
+# same layer at f = 3072 and produces a partial y (summed across GPUs by one
+# all-reduce, not part of this single-GPU build).
+LARGE_DECODE_TP8 = Workload("large-decode-tp8", T=64, d=8192, f=3072)
+LARGE_PREFILL_SKEWED_TP8 = Workload("large-prefill-skewed-tp8", T=16384, d=8192, f=3072, hot_bias=2.0)
+SHARD_WORKLOADS = {w.name: w for w in (LARGE_DECODE_TP8, LARGE_PREFILL_SKEWED_TP8)}
+ALL_WORKLOADS = {**WORKLOADS, **DENSE_WORKLOADS, **SHARD_WORKLOADS}
 
 TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}
 
