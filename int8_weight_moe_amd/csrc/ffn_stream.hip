@@ -651,13 +651,14 @@ __global__ __launch_bounds__(W * kWave) void ffn_stream_shared_dn_kernel(
 
 // y_rows[r, c] = ((part[0] + part[1]) + ...) + part[KS-1], times the channel
 // scale of row r's expert (unscaled encodings: 1); rows of no expert are left
-// as they are. One workgroup per (row, 1024 channels), four channels a thread.
+// as they are. One workgroup per (row, 1024 channels), four channels a thread;
+// rows run along the grid's x axis (up to 2^26 of them), channel blocks along y.
 template <bool kScaleBf16, bool kScaled>
 __global__ __launch_bounds__(256) void split_down_reduce_kernel(const float* __restrict__ part, int KS, int S, int N,
                                                                 const int32_t* __restrict__ offsets, int E,
                                                                 const void* __restrict__ S0,
                                                                 float* __restrict__ y_rows) {
-  const int r = blockIdx.y;
+  const int r = blockIdx.x;
   const int lane = threadIdx.x & 63;
   int o0 = 0, o1 = 0;
   if (lane < E) {
@@ -667,7 +668,7 @@ __global__ __launch_bounds__(256) void split_down_reduce_kernel(const float* __r
   const uint64_t hit = __ballot(lane < E && r >= o0 && r < o1);
   if (hit == 0) return;   // the same for the whole workgroup
   const int e = __ffsll((unsigned long long)hit) - 1;
-  const int c = (blockIdx.x * 256 + threadIdx.x) * 4;
+  const int c = (blockIdx.y * 256 + threadIdx.x) * 4;
   if (c >= N) return;
   const long o = (long)r * N + c;
   f32x4 v = *reinterpret_cast<const f32x4*>(part + o);
@@ -769,7 +770,7 @@ hipError_t launch_stream_shared_dn(const FfnArgs& a, int KS, hipStream_t stream)
                      stream, static_cast<const __bf16*>(a.h), a.w_down, a.offsets, a.E, a.d, a.f, a.S, KS, a.part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const dim3 rgrid((unsigned)((a.d + 1023) / 1024), (unsigned)a.S);
+  const dim3 rgrid((unsigned)a.S, (unsigned)((a.d + 1023) / 1024));
   if (!WFormat<F>::kScaled) {
     hipLaunchKernelGGL((split_down_reduce_kernel<true, false>), rgrid, dim3(256), 0, stream, a.part, KS, a.S, a.d,
                        a.offsets, a.E, a.s_down, a.y_rows);
