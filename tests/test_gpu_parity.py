@@ -92,6 +92,19 @@ def test_route_matches_oracle(T, d, E, K, act, bias):
     check_routing(ids.cpu().numpy(), gw.cpu().numpy(), logits, K)
 
 
+def test_route_does_not_depend_on_the_batch():
+    """Small batches (<= 64 tokens) are scored one token per workgroup, larger ones
+    sixteen per workgroup: a token's ids and weights must be the same bit for bit."""
+    w = workloads.Workload("rb", T=100, d=1024, f=64, E=16, K=2, act="bf16", seed=9)
+    x = workloads.draw_activations(w).cuda()
+    wr = workloads.draw_router(w)[0].cuda()
+    ids, gw = moe_route(x, wr, None, 2)
+    ids_a, gw_a = moe_route(x[:64].contiguous(), wr, None, 2)
+    ids_b, gw_b = moe_route(x[64:].contiguous(), wr, None, 2)
+    torch.cuda.synchronize()
+    assert torch.equal(ids, torch.cat([ids_a, ids_b])) and torch.equal(gw, torch.cat([gw_a, gw_b]))
+
+
 def test_route_exact_ties_go_to_lower_index():
     T, d, E = 16, 128, 8
     x = torch.randn(T, d, generator=torch.Generator().manual_seed(1)).to(torch.bfloat16)
