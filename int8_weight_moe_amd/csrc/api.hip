@@ -135,6 +135,8 @@ moe::FfnArgs ffn_args(const moe_shape* s, const void* x, const int32_t* offsets,
   a.h = h;
   a.y_rows = y_rows;
   a.part = nullptr;
+  a.ids = nullptr;
+  a.perm_offsets = a.perm_sorted = a.perm_s2r = nullptr;
   a.T = s->T;
   a.d = s->d;
   a.f = s->f;
@@ -376,11 +378,22 @@ moe_status moe_forward(const moe_shape* s, const void* x, const void* router_w, 
   hipError_t e = moe::launch_router(x, router_w, router_bias, s->T, s->d, s->E, s->K, s->act_dtype == MOE_BF16,
                                     ids, wts, stream);
   if (e != hipSuccess) return hip_fail(e, "router launch");
-  e = moe::launch_permute(ids, s->T * s->K, s->E, offsets, sorted, s2r, stream);
-  if (e != hipSuccess) return hip_fail(e, "permute launch");
   moe::FfnArgs a = ffn_args(s, x, offsets, sorted, w_gate, w_up, w_down, s_gate, s_up, s_down, y_rows, h);
   if (L.part_bytes) a.part = reinterpret_cast<float*>(ws + L.part);
-  st = run_gate_up(s, a, stream);
+  if (use_stream(s) && moe::stream_gate_up_takes_ids((long)s->T * s->K, s->E)) {
+    // at most 64 slots: the gate/up pass derives the permutation from the ids
+    // and writes it for the down pass and the combine (one launch fewer)
+    a.ids = ids;
+    a.perm_offsets = offsets;
+    a.perm_sorted = sorted;
+    a.perm_s2r = s2r;
+    st = run_gate_up(s, a, stream);
+    a.ids = nullptr;
+  } else {
+    e = moe::launch_permute(ids, s->T * s->K, s->E, offsets, sorted, s2r, stream);
+    if (e != hipSuccess) return hip_fail(e, "permute launch");
+    st = run_gate_up(s, a, stream);
+  }
   if (st != MOE_OK) return st;
   st = run_down(s, a, stream);
   if (st != MOE_OK) return st;

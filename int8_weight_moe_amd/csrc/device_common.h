@@ -95,25 +95,98 @@ __device__ __forceinline__ bool find_row_tile(const int32_t* __restrict__ offset
   return true;
 }
 
+// The experts' row segments, one expert per lane (lanes >= E hold empty
+// segments), and the mask of the experts that have rows.
+struct ExpertSegments {
+  int o0, o1;
+  uint64_t touched;
+};
+
+__device__ __forceinline__ ExpertSegments load_segments(const int32_t* __restrict__ offsets, int E) {
+  const int lane = threadIdx.x & (kWave - 1);
+  ExpertSegments g{0, 0, 0};
+  if (lane < E) {
+    g.o0 = offsets[lane];
+    g.o1 = offsets[lane + 1];
+  }
+  g.touched = __ballot(lane < E && g.o1 > g.o0);
+  return g;
+}
+
 // The te-th expert (in index order) among those with at least one row: its
 // index, first row and row count. Returns false when fewer experts have rows.
-__device__ __forceinline__ bool find_touched_expert(const int32_t* __restrict__ offsets, int E, int te, int& e,
-                                                    int& row0, int& nrows) {
+__device__ __forceinline__ bool touched_expert(const ExpertSegments& g, int te, int& e, int& row0, int& nrows) {
   const int lane = threadIdx.x & (kWave - 1);
-  int o0 = 0, o1 = 0;
-  if (lane < E) {
-    o0 = offsets[lane];
-    o1 = offsets[lane + 1];
-  }
-  const uint64_t touched = __ballot(lane < E && o1 > o0);
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
-  const uint64_t hit = __ballot(lane < E && o1 > o0 && __popcll(touched & below) == te);
+  const bool mine = (g.touched >> lane) & 1ull;
+  const uint64_t hit = __ballot(mine && __popcll(g.touched & below) == te);
   if (hit == 0) return false;
   const int x = __builtin_amdgcn_readfirstlane(__ffsll((unsigned long long)hit) - 1);
   e = x;
-  row0 = __builtin_amdgcn_readfirstlane(__shfl(o0, x));
-  nrows = __builtin_amdgcn_readfirstlane(__shfl(o1, x) - row0);
+  row0 = __builtin_amdgcn_readfirstlane(__shfl(g.o0, x));
+  nrows = __builtin_amdgcn_readfirstlane(__shfl(g.o1, x) - row0);
   return true;
+}
+
+__device__ __forceinline__ bool find_touched_expert(const int32_t* __restrict__ offsets, int E, int te, int& e,
+                                                    int& row0, int& nrows) {
+  return touched_expert(load_segments(offsets, E), te, e, row0, nrows);
+}
+
+// ---------------------------------------------------------------- permutation of at most 64 slots
+// For S <= 64 slots one wave holds every expert id (lane s: slot s, -1 past
+// S), so a kernel can derive the permutation itself instead of reading it.
+// It is the one the permutation kernel writes: experts in index order, slots
+// ascending inside an expert, ids outside [0, E) not placed.
+
+// Position of the k-th (from 0) set bit of m; k < popcount(m).
+__device__ __forceinline__ int select_bit(uint64_t m, int k) {
+  for (int i = 0; i < k; ++i) m &= m - 1;
+  return __ffsll((unsigned long long)m) - 1;
+}
+
+// The experts' row segments (as load_segments) from the wave's ids.
+__device__ __forceinline__ ExpertSegments segments_from_ids(int id, int E) {
+  const int lane = threadIdx.x & (kWave - 1);
+  int cnt = 0;   // lane x: rows of expert x
+  for (int x = 0; x < E; ++x) {
+    const uint64_t m = __ballot(id == x);
+    if (lane == x) cnt = __popcll(m);
+  }
+  int incl = cnt;
+#pragma unroll
+  for (int dd = 1; dd < kWave; dd <<= 1) {
+    const int v = __shfl_up(incl, dd);
+    if (lane >= dd) incl += v;
+  }
+  ExpertSegments g;
+  g.o0 = incl - cnt;
+  g.o1 = incl;
+  g.touched = __ballot(lane < E && cnt > 0);
+  return g;
+}
+
+// Writes the permutation (expert_offsets [E+1], sorted_slots [S],
+// slot_to_row [S]) from the wave's ids and segments; one wave calls it.
+__device__ __forceinline__ void write_permutation(int id, const ExpertSegments& g, int E, int S,
+                                                  int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_slots,
+                                                  int32_t* __restrict__ slot_to_row) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+  if (lane < E) offsets[lane] = g.o0;
+  const int total = __builtin_amdgcn_readlane(g.o1, E - 1);
+  if (lane == 0) offsets[E] = total;
+  int row = -1, slot = -1;
+  for (int x = 0; x < E; ++x) {
+    const uint64_t m = __ballot(id == x);
+    const int lo = __builtin_amdgcn_readlane(g.o0, x), hi = __builtin_amdgcn_readlane(g.o1, x);
+    if (id == x) row = lo + __popcll(m & below);
+    if (lane >= lo && lane < hi) slot = select_bit(m, lane - lo);
+  }
+  if (lane < S) {
+    slot_to_row[lane] = row;
+    sorted_slots[lane] = slot;
+  }
 }
 
 // ---------------------------------------------------------------- conversions

@@ -131,12 +131,17 @@ constexpr int stream_block_waves(int KS) { return KS > 1 ? KS : kStreamWaves; }
 
 // A workgroup holds stream_block_waves(KS)/KS items; wave w works on item
 // w/KS and streams the (w%KS)-th slice of its reduction axis.
+// Gate/up pass with `ids` (S <= 64 slots): the rows and their source tokens
+// come from the expert ids themselves (one wave holds them all) instead of a
+// permutation in memory, and wave 0 of workgroup 0 writes that permutation
+// (perm_*) for the passes after it; offsets and sorted_slots are unused.
 template <bool kGateUp, typename Act, bool kScaleBf16, int F, int NG, int RB, int P, int KS>
 __global__ __launch_bounds__(stream_block_waves(KS) * kWave) void ffn_stream_kernel(
     const Act* __restrict__ X, const int32_t* __restrict__ sorted_slots, int topk,
     const int8_t* __restrict__ W0, const int8_t* __restrict__ W1, const void* __restrict__ S0,
     const void* __restrict__ S1, const int32_t* __restrict__ offsets, int E, int N, int Kd,
-    void* __restrict__ out) {
+    void* __restrict__ out, const int32_t* __restrict__ ids, int S, int32_t* __restrict__ perm_offsets,
+    int32_t* __restrict__ perm_sorted, int32_t* __restrict__ perm_s2r) {
   constexpr int NMAT = kGateUp ? 2 : 1;
   using WF = WFormat<F>;
   constexpr int PPS = WF::kPieces;  // 1 KiB blocks per group and step
@@ -156,9 +161,19 @@ __global__ __launch_bounds__(stream_block_waves(KS) * kWave) void ffn_stream_ker
   const int te = item / gpe;
   const int grp = item - te * gpe;
   int e, row0, nrows;
+  int my_id = -1;          // ids mode: slot `lane`'s expert
+  uint64_t e_slots = 0;    // ids mode: the slots of expert e
   // With KS > 1 the workgroup is one item: every wave takes this return, the
   // row loop and the barriers below together.
-  if (!find_touched_expert(offsets, E, te, e, row0, nrows)) return;
+  if (kGateUp && ids) {
+    my_id = lane < S ? ids[lane] : -1;
+    const ExpertSegments segs = segments_from_ids(my_id, E);
+    if (blockIdx.x == 0 && wave == 0) write_permutation(my_id, segs, E, S, perm_offsets, perm_sorted, perm_s2r);
+    if (!touched_expert(segs, te, e, row0, nrows)) return;
+    e_slots = __ballot(my_id == e);
+  } else if (!find_touched_expert(offsets, E, te, e, row0, nrows)) {
+    return;
+  }
 
   const int ch_base = grp * 16 * NG;
   // first 1 KiB block of each 16-channel group (tiled layout), this lane's piece
@@ -201,7 +216,8 @@ __global__ __launch_bounds__(stream_block_waves(KS) * kWave) void ffn_stream_ker
       long src = 0;
       if (aok[rb]) {
         if constexpr (kGateUp) {
-          src = (long)(sorted_slots[row0 + r] / topk) * Kd;
+          const int slot = ids ? select_bit(e_slots, r) : sorted_slots[row0 + r];
+          src = (long)(slot / topk) * Kd;
         } else {
           src = (long)(row0 + r) * Kd;
         }
@@ -692,11 +708,13 @@ hipError_t launch_stream_pass_ks(const FfnArgs& a, long items, hipStream_t strea
   if constexpr (kGateUp) {
     hipLaunchKernelGGL((ffn_stream_kernel<true, Act, kScaleBf16, F, NG, RB, P, KS>), grid, block, 0, stream,
                        static_cast<const Act*>(a.x), a.sorted_slots, a.K, a.w_gate, a.w_up, a.s_gate, a.s_up,
-                       a.offsets, a.E, N, Kd, static_cast<void*>(a.h));
+                       a.offsets, a.E, N, Kd, static_cast<void*>(a.h), a.ids, a.S, a.perm_offsets, a.perm_sorted,
+                       a.perm_s2r);
   } else {
     hipLaunchKernelGGL((ffn_stream_kernel<false, __bf16, kScaleBf16, F, NG, RB, P, KS>), grid, block, 0, stream,
                        static_cast<const __bf16*>(a.h), a.sorted_slots, a.K, a.w_down, nullptr, a.s_down,
-                       nullptr, a.offsets, a.E, N, Kd, static_cast<void*>(a.y_rows));
+                       nullptr, a.offsets, a.E, N, Kd, static_cast<void*>(a.y_rows), nullptr, a.S, nullptr, nullptr,
+                       nullptr);
   }
   return hipGetLastError();
 }
@@ -792,6 +810,7 @@ hipError_t launch_stream_shared_dn(const FfnArgs& a, int KS, hipStream_t stream)
 // reduction split when the caller gives it the partial-sum planes.
 template <bool kGateUp, typename Act, bool kScaleBf16, int F>
 hipError_t launch_stream_pass(const FfnArgs& a, hipStream_t stream) {
+  if (a.ids && !(kGateUp && stream_gate_up_takes_ids(a.S, a.E))) return hipErrorInvalidValue;
   if ((long)a.S > 32L * a.E) {
     if constexpr (kGateUp && sizeof(Act) == 2) {
       if (MOE_STREAM_SHARED_GU && (uint64_t)a.T * a.d * 2 < (1ull << 32))
@@ -833,6 +852,8 @@ hipError_t dispatch_stream(const FfnArgs& a, hipStream_t stream) {
 }  // namespace
 
 int stream_down_planes(long S, int d, int f, int E) { return shared_down_planes(S, d, f, E); }
+
+bool stream_gate_up_takes_ids(long S, int E) { return S <= kWave && S <= 32L * E; }
 
 hipError_t launch_stream_gate_up(const FfnArgs& a, hipStream_t stream) { return dispatch_stream<true>(a, stream); }
 hipError_t launch_stream_down(const FfnArgs& a, hipStream_t stream) { return dispatch_stream<false>(a, stream); }

@@ -31,6 +31,12 @@ struct FfnArgs {
   __bf16* h;                  // [S, f] scratch
   float* y_rows;              // [S, d] out
   float* part;                // [planes, S, d] scratch of a down pass split over workgroups, or null
+  // gate/up from the expert ids (S <= 64, 32-row stream pass): ids [S] in,
+  // the permutation (offsets, sorted_slots, slot_to_row) out; null otherwise
+  const int32_t* ids;
+  int32_t* perm_offsets;
+  int32_t* perm_sorted;
+  int32_t* perm_s2r;
   int T, d, f, E, K, S;
 };
 
@@ -42,6 +48,9 @@ hipError_t launch_stream_down(const FfnArgs& a, hipStream_t stream);
 // stream down pass splits its reduction over workgroups; 0: it does not. With
 // part null the pass keeps the split inside one workgroup, with the same result.
 int stream_down_planes(long S, int d, int f, int E);
+// Whether the stream gate/up pass can take the expert ids instead of a
+// permutation (FfnArgs::ids): at most 64 slots on the 32-row variant.
+bool stream_gate_up_takes_ids(long S, int E);
 // Tiled MFMA schedule for many rows per expert (prefill). bf16 and fp8
 // weights need bf16 activations and dma_offsets_fit(T, S, d, f, bytes per
 // weight); int8 weights take any shape.

@@ -251,6 +251,35 @@ def test_forward_equals_staged_calls_bitwise(path):
     assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
 
 
+@pytest.mark.parametrize("T,d,f,E,K,act", [
+    (1, 128, 192, 16, 2, "bf16"), (32, 256, 384, 16, 2, "bf16"), (64, 128, 128, 64, 1, "bf16"),
+    (8, 128, 256, 8, 8, "bf16"), (20, 192, 256, 1, 1, "bf16"), (32, 256, 512, 16, 2, "f32"),
+    (21, 128, 192, 5, 3, "bf16"),
+])
+def test_forward_small_batch_equals_staged(T, d, f, E, K, act):
+    """At most 64 slots: moe_forward lets the gate/up pass derive the permutation
+    from the expert ids (no permutation launch); it must equal the staged calls,
+    which use moe_permute, bit for bit, and match the oracle."""
+    scale = act
+    w, x, wr, b, W = _case(T, d, f, E, K, act, scale, bias=[1.5] + [0.0] * (E - 1) if E > 1 else None, seed=T + E)
+    ex = experts_to_device(W, TDT[scale])
+    xg, wrg = x.cuda(), wr.cuda()
+    bg = None if b is None else b.cuda()
+    y, ids, gw = moe_forward(xg, wrg, bg, ex, K, path=MOE_PATH_STREAM)
+    y_auto, _, _ = moe_forward(xg, wrg, bg, ex, K)
+    ids2, gw2 = moe_route(xg, wrg, bg, K)
+    off, ss, s2r = moe_permute(ids2, E)
+    rows = moe_expert_ffn(xg, off, ss, ex, K, path=MOE_PATH_STREAM)
+    y2 = moe_combine(rows, s2r, gw2, TDT[act])
+    torch.cuda.synchronize()
+    assert torch.equal(ids, ids2) and torch.equal(gw, gw2)
+    assert torch.equal(y, y2) and torch.equal(y, y_auto)
+    logits = omoe.router_logits(np64(x), np64(wr), None if b is None else np64(b))
+    check_routing(ids.cpu().numpy(), gw.cpu().numpy(), logits, K)
+    ref = omoe.moe_forward(np64(x), np64(wr), None if b is None else np64(b), W, K, ids=ids.cpu().numpy())
+    assert_close_to_oracle(np64(y), ref["y"], f"small batch T={T} E={E} K={K} {act}")
+
+
 @pytest.mark.parametrize("path", PATHS)
 def test_forward_deterministic_and_token_permutation_equivariant(path):
     w, x, wr, b, W = _case(192, 256, 256, 16, 2, "bf16", "bf16", seed=6)
