@@ -381,7 +381,7 @@ moe_status moe_forward(const moe_shape* s, const void* x, const void* router_w, 
   moe::FfnArgs a = ffn_args(s, x, offsets, sorted, w_gate, w_up, w_down, s_gate, s_up, s_down, y_rows, h);
   if (L.part_bytes) a.part = reinterpret_cast<float*>(ws + L.part);
   if (use_stream(s) && moe::stream_gate_up_takes_ids((long)s->T * s->K, s->E)) {
-    // at most 64 slots: the gate/up pass derives the permutation from the ids
+    // at most 256 slots: the gate/up pass derives the permutation from the ids
     // and writes it for the down pass and the combine (one launch fewer)
     a.ids = ids;
     a.perm_offsets = offsets;

@@ -133,11 +133,30 @@ __device__ __forceinline__ bool find_touched_expert(const int32_t* __restrict__ 
   return touched_expert(load_segments(offsets, E), te, e, row0, nrows);
 }
 
-// ---------------------------------------------------------------- permutation of at most 64 slots
-// For S <= 64 slots one wave holds every expert id (lane s: slot s, -1 past
-// S), so a kernel can derive the permutation itself instead of reading it.
-// It is the one the permutation kernel writes: experts in index order, slots
-// ascending inside an expert, ids outside [0, E) not placed.
+// ---------------------------------------------------------------- permutation of at most 256 slots
+// For S <= 64*kIdChunks slots one wave holds every expert id (chunk c, lane
+// l: slot 64c + l; -1 past S), so a kernel can derive the permutation itself
+// instead of reading it. It is the one the permutation kernel writes: experts
+// in index order, slots ascending inside an expert, ids outside [0, E) not
+// placed.
+constexpr int kIdChunks = 4;
+
+struct WaveIds {
+  int id[kIdChunks];
+  int chunks;   // ceil(S / 64)
+};
+
+__device__ __forceinline__ WaveIds load_wave_ids(const int32_t* __restrict__ ids, int S) {
+  const int lane = threadIdx.x & (kWave - 1);
+  WaveIds w;
+  w.chunks = (S + kWave - 1) / kWave;
+#pragma unroll
+  for (int c = 0; c < kIdChunks; ++c) {
+    const int sl = c * kWave + lane;
+    w.id[c] = (c < w.chunks && sl < S) ? ids[sl] : -1;
+  }
+  return w;
+}
 
 // Position of the k-th (from 0) set bit of m; k < popcount(m).
 __device__ __forceinline__ int select_bit(uint64_t m, int k) {
@@ -145,13 +164,34 @@ __device__ __forceinline__ int select_bit(uint64_t m, int k) {
   return __ffsll((unsigned long long)m) - 1;
 }
 
+// The slots of expert x, one 64-slot chunk per mask; all lanes must call it
+// (ballots).
+__device__ __forceinline__ void expert_masks(const WaveIds& w, int x, uint64_t (&m)[kIdChunks]) {
+#pragma unroll
+  for (int c = 0; c < kIdChunks; ++c) m[c] = (c < w.chunks) ? __ballot(w.id[c] == x) : 0ull;
+}
+
+// The k-th (from 0) slot among the masks, k < their total popcount. Lane-local.
+__device__ __forceinline__ int select_slot(const uint64_t (&m)[kIdChunks], int k) {
+#pragma unroll
+  for (int c = 0; c < kIdChunks; ++c) {
+    const int n = __popcll(m[c]);
+    if (k < n) return c * kWave + select_bit(m[c], k);
+    k -= n;
+  }
+  return -1;
+}
+
 // The experts' row segments (as load_segments) from the wave's ids.
-__device__ __forceinline__ ExpertSegments segments_from_ids(int id, int E) {
+__device__ __forceinline__ ExpertSegments segments_from_ids(const WaveIds& w, int E) {
   const int lane = threadIdx.x & (kWave - 1);
   int cnt = 0;   // lane x: rows of expert x
   for (int x = 0; x < E; ++x) {
-    const uint64_t m = __ballot(id == x);
-    if (lane == x) cnt = __popcll(m);
+    int n = 0;
+#pragma unroll
+    for (int c = 0; c < kIdChunks; ++c)
+      if (c < w.chunks) n += __popcll(__ballot(w.id[c] == x));
+    if (lane == x) cnt = n;
   }
   int incl = cnt;
 #pragma unroll
@@ -168,7 +208,7 @@ __device__ __forceinline__ ExpertSegments segments_from_ids(int id, int E) {
 
 // Writes the permutation (expert_offsets [E+1], sorted_slots [S],
 // slot_to_row [S]) from the wave's ids and segments; one wave calls it.
-__device__ __forceinline__ void write_permutation(int id, const ExpertSegments& g, int E, int S,
+__device__ __forceinline__ void write_permutation(const WaveIds& w, const ExpertSegments& g, int E, int S,
                                                   int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_slots,
                                                   int32_t* __restrict__ slot_to_row) {
   const int lane = threadIdx.x & (kWave - 1);
@@ -176,16 +216,32 @@ __device__ __forceinline__ void write_permutation(int id, const ExpertSegments& 
   if (lane < E) offsets[lane] = g.o0;
   const int total = __builtin_amdgcn_readlane(g.o1, E - 1);
   if (lane == 0) offsets[E] = total;
-  int row = -1, slot = -1;
+  int row[kIdChunks], slot[kIdChunks];
+#pragma unroll
+  for (int c = 0; c < kIdChunks; ++c) row[c] = slot[c] = -1;
   for (int x = 0; x < E; ++x) {
-    const uint64_t m = __ballot(id == x);
     const int lo = __builtin_amdgcn_readlane(g.o0, x), hi = __builtin_amdgcn_readlane(g.o1, x);
-    if (id == x) row = lo + __popcll(m & below);
-    if (lane >= lo && lane < hi) slot = select_bit(m, lane - lo);
+    uint64_t m[kIdChunks];
+    expert_masks(w, x, m);
+    int before = 0;   // rows of expert x in the chunks before c
+#pragma unroll
+    for (int c = 0; c < kIdChunks; ++c) {
+      if (w.id[c] == x) row[c] = lo + before + __popcll(m[c] & below);
+      before += __popcll(m[c]);
+    }
+#pragma unroll
+    for (int c = 0; c < kIdChunks; ++c) {
+      const int r = c * kWave + lane;   // sorted row held by this lane
+      if (r >= lo && r < hi) slot[c] = select_slot(m, r - lo);
+    }
   }
-  if (lane < S) {
-    slot_to_row[lane] = row;
-    sorted_slots[lane] = slot;
+#pragma unroll
+  for (int c = 0; c < kIdChunks; ++c) {
+    const int sl = c * kWave + lane;
+    if (c < w.chunks && sl < S) {
+      slot_to_row[sl] = row[c];
+      sorted_slots[sl] = slot[c];
+    }
   }
 }
 

@@ -131,7 +131,7 @@ constexpr int stream_block_waves(int KS) { return KS > 1 ? KS : kStreamWaves; }
 
 // A workgroup holds stream_block_waves(KS)/KS items; wave w works on item
 // w/KS and streams the (w%KS)-th slice of its reduction axis.
-// Gate/up pass with `ids` (S <= 64 slots): the rows and their source tokens
+// Gate/up pass with `ids` (S <= 256 slots): the rows and their source tokens
 // come from the expert ids themselves (one wave holds them all) instead of a
 // permutation in memory, and wave 0 of workgroup 0 writes that permutation
 // (perm_*) for the passes after it; offsets and sorted_slots are unused.
@@ -161,16 +161,15 @@ __global__ __launch_bounds__(stream_block_waves(KS) * kWave) void ffn_stream_ker
   const int te = item / gpe;
   const int grp = item - te * gpe;
   int e, row0, nrows;
-  int my_id = -1;          // ids mode: slot `lane`'s expert
-  uint64_t e_slots = 0;    // ids mode: the slots of expert e
+  uint64_t e_slots[kIdChunks] = {};   // ids mode: the slots of expert e
   // With KS > 1 the workgroup is one item: every wave takes this return, the
   // row loop and the barriers below together.
   if (kGateUp && ids) {
-    my_id = lane < S ? ids[lane] : -1;
-    const ExpertSegments segs = segments_from_ids(my_id, E);
-    if (blockIdx.x == 0 && wave == 0) write_permutation(my_id, segs, E, S, perm_offsets, perm_sorted, perm_s2r);
+    const WaveIds wid = load_wave_ids(ids, S);
+    const ExpertSegments segs = segments_from_ids(wid, E);
+    if (blockIdx.x == 0 && wave == 0) write_permutation(wid, segs, E, S, perm_offsets, perm_sorted, perm_s2r);
     if (!touched_expert(segs, te, e, row0, nrows)) return;
-    e_slots = __ballot(my_id == e);
+    expert_masks(wid, e, e_slots);
   } else if (!find_touched_expert(offsets, E, te, e, row0, nrows)) {
     return;
   }
@@ -216,7 +215,7 @@ __global__ __launch_bounds__(stream_block_waves(KS) * kWave) void ffn_stream_ker
       long src = 0;
       if (aok[rb]) {
         if constexpr (kGateUp) {
-          const int slot = ids ? select_bit(e_slots, r) : sorted_slots[row0 + r];
+          const int slot = ids ? select_slot(e_slots, r) : sorted_slots[row0 + r];
           src = (long)(slot / topk) * Kd;
         } else {
           src = (long)(row0 + r) * Kd;
@@ -853,7 +852,7 @@ hipError_t dispatch_stream(const FfnArgs& a, hipStream_t stream) {
 
 int stream_down_planes(long S, int d, int f, int E) { return shared_down_planes(S, d, f, E); }
 
-bool stream_gate_up_takes_ids(long S, int E) { return S <= kWave && S <= 32L * E; }
+bool stream_gate_up_takes_ids(long S, int E) { return S <= (long)kWave * kIdChunks && S <= 32L * E; }
 
 hipError_t launch_stream_gate_up(const FfnArgs& a, hipStream_t stream) { return dispatch_stream<true>(a, stream); }
 hipError_t launch_stream_down(const FfnArgs& a, hipStream_t stream) { return dispatch_stream<false>(a, stream); }

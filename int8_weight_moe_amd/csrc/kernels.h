@@ -31,7 +31,7 @@ struct FfnArgs {
   __bf16* h;                  // [S, f] scratch
   float* y_rows;              // [S, d] out
   float* part;                // [planes, S, d] scratch of a down pass split over workgroups, or null
-  // gate/up from the expert ids (S <= 64, 32-row stream pass): ids [S] in,
+  // gate/up from the expert ids (S <= 256, 32-row stream pass): ids [S] in,
   // the permutation (offsets, sorted_slots, slot_to_row) out; null otherwise
   const int32_t* ids;
   int32_t* perm_offsets;
@@ -49,7 +49,7 @@ hipError_t launch_stream_down(const FfnArgs& a, hipStream_t stream);
 // part null the pass keeps the split inside one workgroup, with the same result.
 int stream_down_planes(long S, int d, int f, int E);
 // Whether the stream gate/up pass can take the expert ids instead of a
-// permutation (FfnArgs::ids): at most 64 slots on the 32-row variant.
+// permutation (FfnArgs::ids): at most 256 slots on the 32-row variant.
 bool stream_gate_up_takes_ids(long S, int E);
 // Tiled MFMA schedule for many rows per expert (prefill). bf16 and fp8
 // weights need bf16 activations and dma_offsets_fit(T, S, d, f, bytes per

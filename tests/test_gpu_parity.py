@@ -254,12 +254,14 @@ def test_forward_equals_staged_calls_bitwise(path):
 @pytest.mark.parametrize("T,d,f,E,K,act", [
     (1, 128, 192, 16, 2, "bf16"), (32, 256, 384, 16, 2, "bf16"), (64, 128, 128, 64, 1, "bf16"),
     (8, 128, 256, 8, 8, "bf16"), (20, 192, 256, 1, 1, "bf16"), (32, 256, 512, 16, 2, "f32"),
-    (21, 128, 192, 5, 3, "bf16"),
+    (21, 128, 192, 5, 3, "bf16"), (64, 256, 384, 16, 2, "bf16"), (100, 128, 256, 16, 2, "bf16"),
+    (256, 128, 192, 8, 1, "bf16"), (85, 128, 128, 64, 3, "bf16"),
 ])
 def test_forward_small_batch_equals_staged(T, d, f, E, K, act):
-    """At most 64 slots: moe_forward lets the gate/up pass derive the permutation
-    from the expert ids (no permutation launch); it must equal the staged calls,
-    which use moe_permute, bit for bit, and match the oracle."""
+    """At most 256 slots (and at most 32 per expert on average): moe_forward lets
+    the gate/up pass derive the permutation from the expert ids (no permutation
+    launch); it must equal the staged calls, which use moe_permute, bit for bit,
+    and match the oracle. Shapes span one to four 64-slot chunks."""
     scale = act
     w, x, wr, b, W = _case(T, d, f, E, K, act, scale, bias=[1.5] + [0.0] * (E - 1) if E > 1 else None, seed=T + E)
     ex = experts_to_device(W, TDT[scale])
