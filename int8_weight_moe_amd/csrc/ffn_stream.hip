@@ -18,7 +18,9 @@
 //     how a lane's pieces become the two operands and which activation
 //     elements pair with them.
 // Items are numbered over the experts that received rows only, so the grid
-// has no idle waves for untouched experts.
+// has no idle waves for untouched experts. For at most 256 slots the gate/up
+// pass can take the expert ids instead of the permutation and write the
+// permutation itself (one launch fewer for a decode step).
 // With few experts (a dense MLP layer: one) there are too few items to keep
 // enough loads in flight, so the reduction axis of each item is cut into KS
 // slices streamed by the KS waves of one workgroup; the slices' fp32 partial
@@ -131,6 +133,7 @@ constexpr int stream_block_waves(int KS) { return KS > 1 ? KS : kStreamWaves; }
 
 // A workgroup holds stream_block_waves(KS)/KS items; wave w works on item
 // w/KS and streams the (w%KS)-th slice of its reduction axis.
+//
 // Gate/up pass with `ids` (S <= 256 slots): the rows and their source tokens
 // come from the expert ids themselves (one wave holds them all) instead of a
 // permutation in memory, and wave 0 of workgroup 0 writes that permutation
