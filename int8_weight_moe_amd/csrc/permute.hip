@@ -52,6 +52,7 @@ __global__ __launch_bounds__(kPermWaves * kWave) void permute_kernel(const int32
     }
 #pragma unroll
     for (int b = 0; b < kBatch; ++b) {
+      if (s0 + 64 * b >= s_end) break;   // past this wave's range (the same for the whole wave)
       for (int e = 0; e < E; ++e) {
         const uint64_t m = __ballot(idv[b] == e);
         if (lane == e) my_count += __popcll(m);
@@ -100,6 +101,7 @@ __global__ __launch_bounds__(kPermWaves * kWave) void permute_kernel(const int32
     }
 #pragma unroll
     for (int b = 0; b < kBatch; ++b) {
+      if (s0 + 64 * b >= s_end) break;   // past this wave's range (the same for the whole wave)
       const int s = s0 + 64 * b + lane;
       const int id = idv[b];
       int pos = -1;
