@@ -28,8 +28,8 @@ pytestmark = pytest.mark.gpu
 def _experts(fmt, w):
     src = workloads.draw_expert_weights(w, "cpu")
     if fmt == "int8":
-        W = quantize_experts_oracle(src, "bf16")
-        return experts_to_device(W, torch.bfloat16), W
+        W = quantize_experts_oracle(src, w.scale)
+        return experts_to_device(W, workloads.TORCH_DTYPE[w.scale]), W
     ws = [src[k].cuda() for k in ("w_gate", "w_up", "w_down")]
     if fmt == "bf16":
         W = {}
@@ -51,28 +51,29 @@ def _base_workspace(T, d, f, E, K):
     return r(S * 4) * 4 + r((E + 1) * 4) + r(S * f * 2) + r(S * d * 4)
 
 
-@pytest.mark.parametrize("fmt", ["int8", "bf16", "fp8"])
+@pytest.mark.parametrize("fmt,act", [("int8", "bf16"), ("bf16", "bf16"), ("fp8", "bf16"), ("int8", "f32")])
 @pytest.mark.parametrize("T,d,f,E,K", [(300, 256, 512, 16, 2), (100, 512, 640, 4, 2), (150, 256, 1024, 2, 2)])
-def test_fused_split_equals_staged_and_oracle(fmt, T, d, f, E, K):
-    w = workloads.Workload("split", T=T, d=d, f=f, E=E, K=K, act="bf16", scale="bf16", weight_src="bf16", seed=21)
+def test_fused_split_equals_staged_and_oracle(fmt, act, T, d, f, E, K):
+    w = workloads.Workload("split", T=T, d=d, f=f, E=E, K=K, act=act, scale=act, weight_src="f32" if act == "f32" else "bf16",
+                           seed=21)
     x = workloads.draw_activations(w)
     wr, _ = workloads.draw_router(w)
     ex, W = _experts(fmt, w)
-    shape = make_shape(T, d, f, E, K, torch.bfloat16, torch.bfloat16, MOE_PATH_STREAM, ex.fmt)
+    shape = make_shape(T, d, f, E, K, workloads.TORCH_DTYPE[act], workloads.TORCH_DTYPE[act], MOE_PATH_STREAM, ex.fmt)
     assert workspace_size(shape) > _base_workspace(T, d, f, E, K), "the split down pass is not planned"
     xg, wrg = x.cuda(), wr.cuda()
     y, ids, gw = moe_forward(xg, wrg, None, ex, K, path=MOE_PATH_STREAM)
     ids2, gw2 = moe_route(xg, wrg, None, K)
     off, ss, s2r = moe_permute(ids2, E)
     rows = moe_expert_ffn(xg, off, ss, ex, K, path=MOE_PATH_STREAM)
-    y2 = moe_combine(rows, s2r, gw2, torch.bfloat16)
+    y2 = moe_combine(rows, s2r, gw2, x.dtype)
     torch.cuda.synchronize()
     assert torch.equal(ids, ids2) and torch.equal(gw, gw2)
-    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+    assert torch.equal(y, y2)
     # the down pass alone, with and without the planes
     h = moe_expert_gate_up(xg, off, ss, ex, K, path=MOE_PATH_STREAM)
-    r_split = moe_expert_down(h, off, ex, T, K, path=MOE_PATH_STREAM)
-    r_in = moe_expert_down(h, off, ex, T, K, path=MOE_PATH_STREAM, split_workspace=False)
+    r_split = moe_expert_down(h, off, ex, T, K, act=x.dtype, path=MOE_PATH_STREAM)
+    r_in = moe_expert_down(h, off, ex, T, K, act=x.dtype, path=MOE_PATH_STREAM, split_workspace=False)
     torch.cuda.synchronize()
     assert torch.equal(r_split, r_in) and torch.equal(r_split, rows)
     counts = np.diff(off.cpu().numpy())
