@@ -283,6 +283,37 @@ def test_forward_small_batch_equals_staged(T, d, f, E, K, act):
 
 
 @pytest.mark.parametrize("path", PATHS)
+def test_forward_degenerate_inputs(path):
+    """Degenerate cases of the method: an expert whose weights are all zero (scale 0,
+    codes 0), a down matrix row that is zero, a token that is all zeros (its router
+    logits are the bias: ties go to the lowest indices), and a token scaled by 100."""
+    T, d, f, E, K = 150, 256, 384, 8, 2
+    w = workloads.Workload("degen", T=T, d=d, f=f, E=E, K=K, act="bf16", scale="bf16", weight_src="bf16", seed=17)
+    x = workloads.draw_activations(w)
+    wr, _ = workloads.draw_router(w)
+    src = workloads.draw_expert_weights(w, "cpu")
+    for k in ("w_gate", "w_up", "w_down"):
+        src[k][3] = 0.0                 # expert 3: all zero
+    src["w_down"][5, 7] = 0.0           # one output channel of expert 5: zero row
+    x[4] = 0.0
+    x[9] = (x[9].float() * 100.0).to(torch.bfloat16)
+    b = torch.zeros(E)
+    b[3] = 3.0                          # route plenty of tokens to the zero expert
+    W = quantize_experts_oracle(src, "bf16")
+    assert np.all(W["s_gate"][3] == 0) and np.all(W["q_gate"][3] == 0)
+    ex = experts_to_device(W, torch.bfloat16)
+    y, ids, gw = moe_forward(x.cuda(), wr.cuda(), b.cuda(), ex, K, path=path)
+    torch.cuda.synchronize()
+    ids_h = ids.cpu().numpy()
+    assert ids_h[4].tolist() == [3, 0]   # zero token: logits = bias, expert 3 first, then the lowest index
+    logits = omoe.router_logits(np64(x), np64(wr), np64(b))
+    check_routing(ids_h, gw.cpu().numpy(), logits, K)
+    ref = omoe.moe_forward(np64(x), np64(wr), np64(b), W, K, ids=ids_h)
+    assert_close_to_oracle(np64(y), ref["y"], f"degenerate inputs path={path}")
+    assert torch.all(y[4] == 0)          # the zero token's output is exactly zero
+
+
+@pytest.mark.parametrize("path", PATHS)
 def test_forward_deterministic_and_token_permutation_equivariant(path):
     w, x, wr, b, W = _case(192, 256, 256, 16, 2, "bf16", "bf16", seed=6)
     ex = experts_to_device(W, torch.bfloat16)
