@@ -66,12 +66,23 @@ constexpr int waitcnt_vm_lgkm0(int vm) { return (vm & 15) | ((vm >> 4) << 14) | 
 // instead of walking the experts one dependent load at a time; every lane of
 // the wave returns the same (wave-uniform) answer.
 
-// Row tile `mt` of the expert-grouped rows, where expert x owns
-// ceil(count_x / BM) consecutive row tiles: its expert, first row and row
-// count. Returns false when mt is past the last tile.
-template <int BM>
-__device__ __forceinline__ bool find_row_tile(const int32_t* __restrict__ offsets, int E, int mt, int& e, int& row0,
-                                              int& nrows) {
+// Tile of this workgroup in the expert-grouped rows x output-channel tiles
+// grid, where expert x owns ceil(count_x / BM) consecutive row tiles.
+//   - The real tile count (row tiles x n_tiles) comes from the offsets, and
+//     block b works on tile (b % xcds) * per_xcd + b / xcds with per_xcd =
+//     ceil(count / xcds) rounded up to a multiple of `grain`: workgroups are
+//     dealt to the XCDs in turn, so every XCD gets a contiguous share of the
+//     real tiles, equal up to the grain (sizing the shares by the grid, which
+//     is launched for the most row tiles the slot count allows, left the last
+//     XCD idle for the tiles that do not exist). The grid must hold
+//     xcds * per_xcd blocks.
+//   - Within a share, groups of GM row tiles take every channel tile before
+//     the next group, so a weight tile is read by GM row tiles in a row.
+// Returns false for blocks past the real tiles; else the expert, first row,
+// row count and channel tile.
+template <int BM, int GM>
+__device__ __forceinline__ bool block_tile(const int32_t* __restrict__ offsets, int E, int n_tiles_n, int xcds,
+                                           int grain, int& e, int& row0, int& nrows, int& nt) {
   const int lane = threadIdx.x & (kWave - 1);
   int o0 = 0, o1 = 0;
   if (lane < E) {
@@ -86,8 +97,20 @@ __device__ __forceinline__ bool find_row_tile(const int32_t* __restrict__ offset
     if (lane >= d) incl += v;
   }
   const int excl = incl - tiles;
+  const int m_tiles = __builtin_amdgcn_readlane(incl, kWave - 1);
+  const int total = m_tiles * n_tiles_n;
+  const int per_xcd = ((total + xcds - 1) / xcds + grain - 1) / grain * grain;
+  const int k = blockIdx.x / xcds;
+  if (k >= per_xcd) return false;
+  const int tile = (blockIdx.x % xcds) * per_xcd + k;
+  if (tile >= total) return false;
+  const int group_tiles = GM * n_tiles_n;
+  const int group = tile / group_tiles;
+  const int in_group = tile - group * group_tiles;
+  const int gm = min(GM, m_tiles - group * GM);   // row tiles in this (possibly last) group
+  const int mt = group * GM + in_group % gm;
+  nt = in_group / gm;
   const uint64_t hit = __ballot(lane < E && mt >= excl && mt < incl);
-  if (hit == 0) return false;
   const int x = __builtin_amdgcn_readfirstlane(__ffsll((unsigned long long)hit) - 1);
   e = x;
   row0 = __builtin_amdgcn_readfirstlane(__shfl(o0, x) + (mt - __shfl(excl, x)) * BM);

@@ -38,6 +38,23 @@ constexpr int kBK = 64;      // reduction step (elements)
 constexpr int kChunks = kBK / 8;  // 16-byte bf16 chunks per LDS row
 constexpr int kXcds = 8;
 
+// Granularity of the XCD shares of a pass's tiles. Gate/up: exact shares
+// (balanced to a tile). Down: whole multiples of the channel-tile count, which
+// on the Large prefill shapes measured 2% faster than exact shares (11.03-11.08
+// against 11.26-11.28 ms) and the same on the Mini ones; exact shares measured
+// 1-2% faster for gate/up.
+__host__ __device__ constexpr int xcd_grain(bool gate_up, int n_tiles_n) { return gate_up ? 1 : n_tiles_n; }
+
+// Blocks a tiled pass launches: room for the largest XCD share of the most row
+// tiles S slots can make (at most one partial tile per expert beyond S / BM);
+// blocks past the real tiles exit at once.
+long tiled_grid_blocks(bool gate_up, long m_tiles_max, int n_tiles_n) {
+  const long total = m_tiles_max * n_tiles_n;
+  const long g = xcd_grain(gate_up, n_tiles_n);
+  const long per_xcd = ((total + kXcds - 1) / kXcds + g - 1) / g * g;
+  return per_xcd * kXcds;
+}
+
 // Tile shape (compile-time; overridable for tuning builds).
 #ifndef MOE_TILE_BM
 #define MOE_TILE_BM 256
@@ -68,7 +85,7 @@ __global__ __launch_bounds__(WM * WN * kWave) void ffn_tiled_kernel(
     const Act* __restrict__ X, const int32_t* __restrict__ sorted_slots, int topk,
     const int8_t* __restrict__ W0, const int8_t* __restrict__ W1, const void* __restrict__ S0,
     const void* __restrict__ S1, const int32_t* __restrict__ offsets, int E, int N, int Kd, int n_tiles_n,
-    int m_tiles, int total_blocks, void* __restrict__ out) {
+    void* __restrict__ out) {
   constexpr int NT = WM * WN * kWave;       // threads
   constexpr int TM = BM / WM;               // rows per wave
   constexpr int TN = BN / WN;               // effective columns per wave
@@ -92,19 +109,9 @@ __global__ __launch_bounds__(WM * WN * kWave) void ffn_tiled_kernel(
   const int li = lane & 15;
   const int lg = lane >> 4;
 
-  // ---- XCD-contiguous tile id, then (expert, row tile, channel tile)
-  const int per_xcd = total_blocks / kXcds;
-  const int tile = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
-  const int group_tiles = GM * n_tiles_n;
-  const int group = tile / group_tiles;
-  const int in_group = tile - group * group_tiles;
-  const int gm = min(GM, m_tiles - group * GM);   // row tiles in this (possibly last) group
-  if (gm <= 0) return;
-  const int mt_global = group * GM + in_group % gm;
-  const int nt = in_group / gm;
-  if (nt >= n_tiles_n) return;
-  int e, row0, nrows;
-  if (!find_row_tile<BM>(offsets, E, mt_global, e, row0, nrows)) return;
+  // ---- XCD-contiguous tile: (expert, row tile, channel tile)
+  int e, row0, nrows, nt;
+  if (!block_tile<BM, GM>(offsets, E, n_tiles_n, kXcds, xcd_grain(kGateUp, n_tiles_n), e, row0, nrows, nt)) return;
   const int n0 = nt * CH_TILE;
 
   // ---- global source pointers of this thread's pieces
@@ -328,7 +335,7 @@ void ffn_tiled_dma_kernel(
     const __bf16* __restrict__ X, const int32_t* __restrict__ sorted_slots, int topk,
     const int8_t* __restrict__ W0, const int8_t* __restrict__ W1, const void* __restrict__ S0,
     const void* __restrict__ S1, const int32_t* __restrict__ offsets, int E, int N, int Kd, int n_tiles_n,
-    int m_tiles, int total_blocks, void* __restrict__ out) {
+    void* __restrict__ out) {
   constexpr int TM = BM / WM, TN = BN / WN, MB = TM / 16, NB = TN / 16;
   static_assert(STAGES == 2 || STAGES == 3, "ring depth");
   using WF = WFormat<F>;
@@ -356,18 +363,8 @@ void ffn_tiled_dma_kernel(
   const int li = lane & 15;
   const int lg = lane >> 4;
 
-  const int per_xcd = total_blocks / kXcds;
-  const int tile = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
-  const int group_tiles = GM * n_tiles_n;
-  const int group = tile / group_tiles;
-  const int in_group = tile - group * group_tiles;
-  const int gm = min(GM, m_tiles - group * GM);
-  if (gm <= 0) return;
-  const int mt_global = group * GM + in_group % gm;
-  const int nt = in_group / gm;
-  if (nt >= n_tiles_n) return;
-  int e, row0, nrows;
-  if (!find_row_tile<BM>(offsets, E, mt_global, e, row0, nrows)) return;
+  int e, row0, nrows, nt;
+  if (!block_tile<BM, GM>(offsets, E, n_tiles_n, kXcds, xcd_grain(kGateUp, n_tiles_n), e, row0, nrows, nt)) return;
   const int n0 = nt * CH_TILE;
 
   // activation sources: instruction j of this wave covers rows 8*(A_INSTR*wave + j) + lane/8;
@@ -582,19 +579,16 @@ hipError_t launch_dma_pass(const FfnArgs& a, hipStream_t stream) {
   const int N = kGateUp ? a.f : a.d;
   const int Kd = kGateUp ? a.d : a.f;
   const int dn_tiles = (N + DCH - 1) / DCH;
-  const long dm_tiles = (long)(a.S + DBM - 1) / DBM + a.E;
-  const long dblocks = (dm_tiles * dn_tiles + kXcds - 1) / kXcds * kXcds;
+  const long dblocks = tiled_grid_blocks(kGateUp, (long)(a.S + DBM - 1) / DBM + a.E, dn_tiles);
   const dim3 dblock(DWM * DWN * kWave);
   if constexpr (kGateUp) {
     hipLaunchKernelGGL((ffn_tiled_dma_kernel<true, kScaleBf16, F, GM, DBM, DBN, DWM, DWN, DST>), dim3((unsigned)dblocks),
                        dblock, 0, stream, static_cast<const __bf16*>(a.x), a.sorted_slots, a.K, a.w_gate, a.w_up,
-                       a.s_gate, a.s_up, a.offsets, a.E, N, Kd, dn_tiles, (int)dm_tiles, (int)dblocks,
-                       static_cast<void*>(a.h));
+                       a.s_gate, a.s_up, a.offsets, a.E, N, Kd, dn_tiles, static_cast<void*>(a.h));
   } else {
     hipLaunchKernelGGL((ffn_tiled_dma_kernel<false, kScaleBf16, F, GM, DBM, DBN, DWM, DWN, DST>), dim3((unsigned)dblocks),
                        dblock, 0, stream, static_cast<const __bf16*>(a.h), a.sorted_slots, a.K, a.w_down, nullptr,
-                       a.s_down, nullptr, a.offsets, a.E, N, Kd, dn_tiles, (int)dm_tiles, (int)dblocks,
-                       static_cast<void*>(a.y_rows));
+                       a.s_down, nullptr, a.offsets, a.E, N, Kd, dn_tiles, static_cast<void*>(a.y_rows));
   }
   return hipGetLastError();
 }
@@ -609,20 +603,17 @@ hipError_t launch_tiled_pass(const FfnArgs& a, hipStream_t stream) {
     return launch_dma_pass<kGateUp, kScaleBf16, kWInt8, MOE_DMA_BN>(a, stream);
   // register-staged kernel (int8 weights only)
   const int n_tiles_n = (N + CH_TILE - 1) / CH_TILE;
-  // row tiles: at most one partial tile per expert beyond S / BM
-  const long m_tiles_max = (long)(a.S + BM - 1) / BM + a.E;
-  long blocks = m_tiles_max * n_tiles_n;
-  blocks = (blocks + kXcds - 1) / kXcds * kXcds;
+  const long blocks = tiled_grid_blocks(kGateUp, (long)(a.S + BM - 1) / BM + a.E, n_tiles_n);
   const dim3 grid((unsigned)blocks);
   const dim3 block(WM * WN * kWave);
   if constexpr (kGateUp) {
     hipLaunchKernelGGL((ffn_tiled_kernel<true, Act, kScaleBf16, BM, BN, WM, WN, GM>), grid, block, 0, stream,
                        static_cast<const Act*>(a.x), a.sorted_slots, a.K, a.w_gate, a.w_up, a.s_gate, a.s_up,
-                       a.offsets, a.E, N, Kd, n_tiles_n, (int)m_tiles_max, (int)blocks, static_cast<void*>(a.h));
+                       a.offsets, a.E, N, Kd, n_tiles_n, static_cast<void*>(a.h));
   } else {
     hipLaunchKernelGGL((ffn_tiled_kernel<false, __bf16, kScaleBf16, BM, BN, WM, WN, GM>), grid, block, 0, stream,
                        static_cast<const __bf16*>(a.h), a.sorted_slots, a.K, a.w_down, nullptr, a.s_down, nullptr,
-                       a.offsets, a.E, N, Kd, n_tiles_n, (int)m_tiles_max, (int)blocks, static_cast<void*>(a.y_rows));
+                       a.offsets, a.E, N, Kd, n_tiles_n, static_cast<void*>(a.y_rows));
   }
   return hipGetLastError();
 }
