@@ -25,8 +25,8 @@
 // groups of GM consecutive row tiles, channel tile by channel tile inside a
 // group, so the tiles that run together share GM activation tiles and a few
 // weight tiles. Workgroup ids are spread so that each XCD (workgroups are dealt
-// round-robin to the 8 XCDs) runs a contiguous range of that order and keeps
-// its operands in its own L2.
+// round-robin to the 8 XCDs) runs a contiguous range of that order, an equal
+// share of the real tiles, and keeps its operands in its own L2.
 #include "device_common.h"
 #include "kernels.h"
 
