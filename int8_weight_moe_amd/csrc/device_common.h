@@ -6,6 +6,12 @@
 
 namespace moe {
 
+// compile-time flag argument for generic lambdas (selects a specialised loop)
+template <bool B>
+struct bool_constant {
+  static constexpr bool value = B;
+};
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));

@@ -454,11 +454,18 @@ __global__ __launch_bounds__(W * kWave) void ffn_stream_shared_gu_kernel(
         if (wave + W * j < A_TOT)
           dma16(X, a_off[j] + (uint32_t)t * 128u, lds_addr(&act[st][0]) + (wave + W * j) * 1024);
     };
-    auto compute = [&](int st) {
+    // One step's MFMAs. A full pass (kFull: all RB row blocks present) has no
+    // branches, so the conversions of one weight piece can overlap the MFMAs of
+    // the previous one. Each accumulator takes its two MFMAs (elements 0-7,
+    // then 8-15 of each lane's piece) in that order, but the first MFMAs of all
+    // row blocks are issued before the second ones, so consecutive MFMAs do not
+    // wait for each other's results.
+    auto compute = [&](int st, auto full) {
+      constexpr bool kFull = decltype(full)::value;
       bf16x8 xf[RB][2];
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
-        if (rb < nrb) {
+        if (kFull || rb < nrb) {
 #pragma unroll
           for (int ks = 0; ks < 2; ++ks) {
             const int row = rb * 16 + li;
@@ -474,28 +481,33 @@ __global__ __launch_bounds__(W * kWave) void ffn_stream_shared_gu_kernel(
           bf16x8 w_lo, w_hi;
           WF::operands(bw[st][ng][m], w_lo, w_hi);
 #pragma unroll
-          for (int rb = 0; rb < RB; ++rb) {
-            if (rb < nrb) {
-              acc[rb][ng][m] = mfma_bf16(w_lo, xf[rb][0], acc[rb][ng][m]);
-              acc[rb][ng][m] = mfma_bf16(w_hi, xf[rb][1], acc[rb][ng][m]);
-            }
+          for (int rb = 0; rb < RB; ++rb)
+            if (kFull || rb < nrb) acc[rb][ng][m] = mfma_bf16(w_lo, xf[rb][0], acc[rb][ng][m]);
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb)
+            if (kFull || rb < nrb) acc[rb][ng][m] = mfma_bf16(w_hi, xf[rb][1], acc[rb][ng][m]);
+        }
+      }
+    };
+    auto main_loop = [&](auto full) {
+#pragma unroll
+      for (int t = 0; t < P - 1; ++t) issue(min(t, nsteps - 1), t);
+      for (int s0 = 0; s0 < nsteps; s0 += P) {
+#pragma unroll
+        for (int j = 0; j < P; ++j) {
+          if (s0 + j < nsteps) {   // the same for every wave
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0((P - 2) * (NWI + A_MIN)));
+            __builtin_amdgcn_s_barrier();
+            issue(min(s0 + j + P - 1, nsteps - 1), (j + P - 1) % P);
+            compute(j, full);
           }
         }
       }
     };
-
-#pragma unroll
-    for (int t = 0; t < P - 1; ++t) issue(min(t, nsteps - 1), t);
-    for (int s0 = 0; s0 < nsteps; s0 += P) {
-#pragma unroll
-      for (int j = 0; j < P; ++j) {
-        if (s0 + j < nsteps) {   // the same for every wave
-          __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0((P - 2) * (NWI + A_MIN)));
-          __builtin_amdgcn_s_barrier();
-          issue(min(s0 + j + P - 1, nsteps - 1), (j + P - 1) % P);
-          compute(j);
-        }
-      }
+    if (nrb == RB) {
+      main_loop(bool_constant<true>{});
+    } else {
+      main_loop(bool_constant<false>{});
     }
     // no load may still be writing the ring when it is reused or the waves exit
     __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
@@ -609,11 +621,13 @@ __global__ __launch_bounds__(W * kWave) void ffn_stream_shared_dn_kernel(
         if (wave + W * j < A_TOT)
           dma16(H, a_off[j] + (uint32_t)t * 128u, lds_addr(&act[st][0]) + (wave + W * j) * 1024);
     };
-    auto compute = [&](int st) {
+    // one step's MFMAs, ordered and specialised as in the shared gate/up kernel
+    auto compute = [&](int st, auto full) {
+      constexpr bool kFull = decltype(full)::value;
       bf16x8 xf[RB][2];
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
-        if (rb < nrb) {
+        if (kFull || rb < nrb) {
 #pragma unroll
           for (int h2 = 0; h2 < 2; ++h2) {
             const int row = rb * 16 + li;
@@ -627,27 +641,32 @@ __global__ __launch_bounds__(W * kWave) void ffn_stream_shared_dn_kernel(
         bf16x8 w_lo, w_hi;
         WF::operands(bw[st][ng], w_lo, w_hi);
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          if (rb < nrb) {
-            acc[rb][ng] = mfma_bf16(w_lo, xf[rb][0], acc[rb][ng]);
-            acc[rb][ng] = mfma_bf16(w_hi, xf[rb][1], acc[rb][ng]);
+        for (int rb = 0; rb < RB; ++rb)
+          if (kFull || rb < nrb) acc[rb][ng] = mfma_bf16(w_lo, xf[rb][0], acc[rb][ng]);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+          if (kFull || rb < nrb) acc[rb][ng] = mfma_bf16(w_hi, xf[rb][1], acc[rb][ng]);
+      }
+    };
+    auto main_loop = [&](auto full) {
+#pragma unroll
+      for (int t = 0; t < P - 1; ++t) issue(min(t, nsteps - 1), t);
+      for (int s0 = 0; s0 < nsteps; s0 += P) {
+#pragma unroll
+        for (int j = 0; j < P; ++j) {
+          if (s0 + j < nsteps) {   // the same for every wave
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0((P - 2) * (NWI + A_MIN)));
+            __builtin_amdgcn_s_barrier();
+            issue(min(s0 + j + P - 1, nsteps - 1), (j + P - 1) % P);
+            compute(j, full);
           }
         }
       }
     };
-
-#pragma unroll
-    for (int t = 0; t < P - 1; ++t) issue(min(t, nsteps - 1), t);
-    for (int s0 = 0; s0 < nsteps; s0 += P) {
-#pragma unroll
-      for (int j = 0; j < P; ++j) {
-        if (s0 + j < nsteps) {   // the same for every wave
-          __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0((P - 2) * (NWI + A_MIN)));
-          __builtin_amdgcn_s_barrier();
-          issue(min(s0 + j + P - 1, nsteps - 1), (j + P - 1) % P);
-          compute(j);
-        }
-      }
+    if (nrb == RB) {
+      main_loop(bool_constant<true>{});
+    } else {
+      main_loop(bool_constant<false>{});
     }
     // no load may still be writing the ring when it is reused or the waves exit
     __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
