@@ -6,10 +6,14 @@
 
 namespace moe {
 
-// compile-time flag argument for generic lambdas (selects a specialised loop)
+// compile-time arguments for generic lambdas (select a specialised loop)
 template <bool B>
 struct bool_constant {
   static constexpr bool value = B;
+};
+template <int I>
+struct int_constant {
+  static constexpr int value = I;
 };
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));

@@ -237,66 +237,94 @@ __global__ __launch_bounds__(stream_block_waves(KS) * kWave) void ffn_stream_ker
 
     // weights are prefetched P-1 steps ahead, activations (small, mostly
     // L2 hits) PA-1 steps ahead; the loop body is unrolled over U steps so
-    // both ring slots are compile-time indices
+    // both ring slots are compile-time indices. The loop is specialised on the
+    // number of 16-row blocks of the pass (NRB; 0: the runtime count nrb), so
+    // the common counts run without branches around the loads and MFMAs.
     constexpr int PA_WANT = RB >= 4 ? MOE_STREAM_PA_WIDE : P;
     constexpr int PA = PA_WANT < P ? PA_WANT : P;
     constexpr int U = ring_unroll(P, PA);
-    uint4 bw[P][NG][NMAT][PPS];
-    bf16x8 av[PA][RB][2];
+    auto run = [&](auto nrbc) {
+      constexpr int NRB = decltype(nrbc)::value;
+      const int nb = NRB > 0 ? NRB : nrb;
+      uint4 bw[P][NG][NMAT][PPS];
+      bf16x8 av[PA][RB][2];
 
-    auto load_w = [&](int s, uint4 (&b)[NG][NMAT][PPS]) {
+      auto load_w = [&](int s, uint4 (&b)[NG][NMAT][PPS]) {
 #pragma unroll
-      for (int ng = 0; ng < NG; ++ng)
+        for (int ng = 0; ng < NG; ++ng)
 #pragma unroll
-        for (int m = 0; m < NMAT; ++m)
+          for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-          for (int q = 0; q < PPS; ++q) b[ng][m][q] = load_nt16(wp[ng][m] + ((long)(s_base + s) * PPS + q) * 1024);
-    };
-    auto load_a = [&](int s, bf16x8 (&a)[RB][2]) {
-      const long off = (long)s * 64;
+            for (int q = 0; q < PPS; ++q) b[ng][m][q] = load_nt16(wp[ng][m] + ((long)(s_base + s) * PPS + q) * 1024);
+      };
+      auto load_a = [&](int s, bf16x8 (&a)[RB][2]) {
+        const long off = (long)s * 64;
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        if (rb < nrb && aok[rb]) {
-          a[rb][0] = load_act8(ap[rb] + off);
-          a[rb][1] = load_act8(ap[rb] + off + WF::kActSecond);
-        } else {
-          a[rb][0] = zero_bf16x8();
-          a[rb][1] = zero_bf16x8();
-        }
-      }
-    };
-    auto compute_step = [&](const uint4 (&b)[NG][NMAT][PPS], const bf16x8 (&a)[RB][2]) {
-#pragma unroll
-      for (int ng = 0; ng < NG; ++ng) {
-#pragma unroll
-        for (int m = 0; m < NMAT; ++m) {
-          bf16x8 w_lo, w_hi;
-          WF::operands(b[ng][m], w_lo, w_hi);
-#pragma unroll
-          for (int rb = 0; rb < RB; ++rb) {
-            if (rb < nrb) {
-              acc[rb][ng][m] = mfma_bf16(w_lo, a[rb][0], acc[rb][ng][m]);
-              acc[rb][ng][m] = mfma_bf16(w_hi, a[rb][1], acc[rb][ng][m]);
+        for (int rb = 0; rb < RB; ++rb) {
+          if (rb < nb) {
+            if (aok[rb]) {
+              a[rb][0] = load_act8(ap[rb] + off);
+              a[rb][1] = load_act8(ap[rb] + off + WF::kActSecond);
+            } else {
+              a[rb][0] = zero_bf16x8();
+              a[rb][1] = zero_bf16x8();
             }
           }
         }
-      }
-    };
+      };
+      // Each accumulator takes its two MFMAs (elements 0-7, then 8-15 of each
+      // lane's piece) in that order. The second MFMAs of channel group ng are
+      // issued after the first ones of group ng+1 (of both matrices, for all
+      // row blocks), so consecutive MFMAs do not wait for each other's results
+      // while only two groups' operands are live.
+      auto compute_step = [&](const uint4 (&b)[NG][NMAT][PPS], const bf16x8 (&a)[RB][2]) {
+        bf16x8 w_hi[NG][NMAT];
+        auto second = [&](int ng) {
+#pragma unroll
+          for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+              if (rb < nb) acc[rb][ng][m] = mfma_bf16(w_hi[ng][m], a[rb][1], acc[rb][ng][m]);
+        };
+#pragma unroll
+        for (int ng = 0; ng < NG; ++ng) {
+          bf16x8 w_lo[NMAT];
+#pragma unroll
+          for (int m = 0; m < NMAT; ++m) WF::operands(b[ng][m], w_lo[m], w_hi[ng][m]);
+#pragma unroll
+          for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+              if (rb < nb) acc[rb][ng][m] = mfma_bf16(w_lo[m], a[rb][0], acc[rb][ng][m]);
+          if (ng > 0) second(ng - 1);
+        }
+        second(NG - 1);
+      };
 
 #pragma unroll
-    for (int j = 0; j < P - 1; ++j)
-      if (j < nsteps) load_w(j, bw[j]);
+      for (int j = 0; j < P - 1; ++j)
+        if (j < nsteps) load_w(j, bw[j]);
 #pragma unroll
-    for (int j = 0; j < PA - 1; ++j)
-      if (j < nsteps) load_a(j, av[j]);
-    for (int s0 = 0; s0 < nsteps; s0 += U) {
+      for (int j = 0; j < PA - 1; ++j)
+        if (j < nsteps) load_a(j, av[j]);
+      for (int s0 = 0; s0 < nsteps; s0 += U) {
 #pragma unroll
-      for (int j = 0; j < U; ++j) {
-        const int s = s0 + j;
-        if (s + P - 1 < nsteps) load_w(s + P - 1, bw[(j + P - 1) % P]);
-        if (s + PA - 1 < nsteps) load_a(s + PA - 1, av[(j + PA - 1) % PA]);
-        if (s < nsteps) compute_step(bw[j % P], av[j % PA]);
+        for (int j = 0; j < U; ++j) {
+          const int s = s0 + j;
+          if (s + P - 1 < nsteps) load_w(s + P - 1, bw[(j + P - 1) % P]);
+          if (s + PA - 1 < nsteps) load_a(s + PA - 1, av[(j + PA - 1) % PA]);
+          if (s < nsteps) compute_step(bw[j % P], av[j % PA]);
+        }
       }
+    };
+    if constexpr (KS > 1) {
+      run(int_constant<0>{});   // one copy: the split's LDS reduction leaves no registers for more
+    } else if (nrb == RB) {
+      run(int_constant<RB>{});
+    } else if (RB == 2 || nrb == 1) {   // RB == 2: the only other count is 1
+      run(int_constant<1>{});
+    } else {
+      run(int_constant<0>{});
     }
 
     if constexpr (KS > 1) {
