@@ -97,6 +97,11 @@ namespace {
 #ifndef MOE_STREAM_P_SHARED
 #define MOE_STREAM_P_SHARED 6
 #endif
+// ring depth of that kernel's reduction-split shape (six waves: the registers
+// of two waves per SIMD leave room for four stages)
+#ifndef MOE_STREAM_P_SHARED_SPLIT
+#define MOE_STREAM_P_SHARED_SPLIT 4
+#endif
 #ifndef MOE_STREAM_SHARED_MIN_WGS
 #define MOE_STREAM_SHARED_MIN_WGS 256
 #endif
@@ -383,18 +388,23 @@ __global__ __launch_bounds__(stream_block_waves(KS) * kWave) void ffn_stream_ker
 // With many rows per expert (a dense MLP layer at decode) every wave of
 // ffn_stream_kernel re-reads the rows' activations from L2 for each step,
 // which costs more vector-memory traffic than the weights it streams. Here a
-// workgroup of W waves holds W consecutive items of one expert (no reduction
-// split): per 64-wide step its waves copy the 64-row activation tile (8 KiB
-// bf16) once into a P-deep LDS ring with direct-to-LDS loads, while each wave
-// streams its own weight blocks into a P-deep register ring; one barrier per
-// step. The tile lands XOR-swizzled by row as in the tiled kernel; each
-// item's MFMAs run in the same order as in ffn_stream_kernel without a
-// reduction split.
+// workgroup of WI*KS waves holds WI consecutive items of one expert, each
+// item's reduction cut into KS equal slices streamed by KS waves (slice-major
+// wave order): per 64-wide step the WI waves of a slice copy that slice's
+// 64-row activation tile (8 KiB bf16) once into the slice's P-deep LDS ring
+// with direct-to-LDS loads, while each wave streams its own weight blocks into
+// a P-deep register ring; one barrier per step. The tile lands XOR-swizzled by
+// row as in the tiled kernel. Without a split (KS = 1) each item's MFMAs run
+// in the same order as in ffn_stream_kernel without a split; with one, slices
+// 1..KS-1 hand their fp32 sums to slice 0 through LDS, which adds them in
+// ascending slice order before the epilogue. The split lets a dense layer,
+// whose items would leave a SIMD of every CU idle, spread the same MFMA and
+// conversion work over all four.
 // Loads per step and wave: NG*2*PPS weight loads, then its share of the 8
 // activation DMAs. Before step s the activations of step s must have landed
 // while the loads of steps s+1..s+P-2 may still be in flight.
-template <bool kScaleBf16, int F, int NG, int W, int P>
-__global__ __launch_bounds__(W * kWave) void ffn_stream_shared_gu_kernel(
+template <bool kScaleBf16, int F, int NG, int WI, int KS, int P>
+__global__ __launch_bounds__(WI * KS * kWave) void ffn_stream_shared_gu_kernel(
     const __bf16* __restrict__ X, const int32_t* __restrict__ sorted_slots, int topk,
     const int8_t* __restrict__ W0, const int8_t* __restrict__ W1, const void* __restrict__ S0,
     const void* __restrict__ S1, const int32_t* __restrict__ offsets, int E, int N, int Kd,
@@ -406,22 +416,26 @@ __global__ __launch_bounds__(W * kWave) void ffn_stream_shared_gu_kernel(
   constexpr int PPS = WF::kPieces;
   constexpr int STAGE = ROWS * 128;          // one step's activation tile
   constexpr int A_TOT = STAGE / 1024;        // its 1 KiB DMA instructions, dealt round-robin to the waves
-  constexpr int A_MAX = (A_TOT + W - 1) / W;
-  constexpr int A_MIN = A_TOT / W;
+  constexpr int A_MAX = (A_TOT + WI - 1) / WI;
+  constexpr int A_MIN = A_TOT / WI;
   constexpr int NWI = NG * NMAT * PPS;       // weight loads per wave and step
   static_assert((P - 2) * (NWI + A_MAX) <= 63, "the vmcnt field holds at most 63");
-  __shared__ __attribute__((aligned(1024))) uint8_t act[P][STAGE];
+  // slices 1..KS-1 pass their sums through the (then idle) rings
+  static_assert((KS - 1) * WI * RB * NG * NMAT * kWave * 16 <= KS * P * STAGE, "reduction fits the rings");
+  __shared__ __attribute__((aligned(1024))) uint8_t act[KS][P][STAGE];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int slice = wave / WI;               // uniform
+  const int witem = wave - slice * WI;
   const int li = lane & 15;
   const int lg = lane >> 4;
 
-  // ---- workgroup -> (expert among the touched ones, W consecutive items)
+  // ---- workgroup -> (expert among the touched ones, WI consecutive items)
   const int gpe = N / (16 * NG);
-  const int wg_per_e = gpe / W;
+  const int wg_per_e = gpe / WI;
   const int te = blockIdx.x / wg_per_e;
-  const int grp = (blockIdx.x - te * wg_per_e) * W + wave;
+  const int grp = (blockIdx.x - te * wg_per_e) * WI + witem;
   int e, row0, nrows;
   if (!find_touched_expert(offsets, E, te, e, row0, nrows)) return;   // the same for every wave of the workgroup
 
@@ -442,23 +456,25 @@ __global__ __launch_bounds__(W * kWave) void ffn_stream_shared_gu_kernel(
       sc[ng][1] = load_scale4<kScaleBf16>(S1, ch);
     }
   }
-  const int nsteps = Kd >> 6;
+  const int nsteps = (Kd >> 6) / KS;         // the launch checks that KS divides the steps
+  const int s_base = slice * nsteps;
 
   for (int p0 = 0; p0 < nrows; p0 += ROWS) {
     const int prow = min(ROWS, nrows - p0);
     const int nrb = (prow + 15) >> 4;
-    // this wave's activation DMAs: tile instruction c = wave + W*j covers rows
-    // 8c..8c+7; lane l writes row 8c + l/8, chunk slot l%8, fetched from the
-    // logical chunk slot ^ (row % 8); rows past the pass re-read row 0
+    // this wave's activation DMAs: tile instruction c = witem + WI*j of its
+    // slice covers rows 8c..8c+7; lane l writes row 8c + l/8, chunk slot l%8,
+    // fetched from the logical chunk slot ^ (row % 8); rows past the pass
+    // re-read row 0
     uint32_t a_off[A_MAX];
 #pragma unroll
     for (int j = 0; j < A_MAX; ++j) {
-      const int c = min(wave + W * j, A_TOT - 1);
+      const int c = min(witem + WI * j, A_TOT - 1);
       const int r = 8 * c + (lane >> 3);
       const int rr = (r < prow) ? r : 0;
       const uint32_t src_row = (uint32_t)(sorted_slots[row0 + p0 + rr] / topk);
       const int chunk = (lane & 7) ^ (r & 7);
-      a_off[j] = (src_row * (uint32_t)Kd + (uint32_t)(chunk * 8)) * 2u;
+      a_off[j] = (src_row * (uint32_t)Kd + (uint32_t)(s_base * 64 + chunk * 8)) * 2u;
     }
 
     f32x4 acc[RB][NG][NMAT];
@@ -476,11 +492,11 @@ __global__ __launch_bounds__(W * kWave) void ffn_stream_shared_gu_kernel(
 #pragma unroll
         for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-          for (int q = 0; q < PPS; ++q) bw[st][ng][m][q] = load_nt16(wp[ng][m] + ((long)t * PPS + q) * 1024);
+          for (int q = 0; q < PPS; ++q) bw[st][ng][m][q] = load_nt16(wp[ng][m] + ((long)(s_base + t) * PPS + q) * 1024);
 #pragma unroll
       for (int j = 0; j < A_MAX; ++j)
-        if (wave + W * j < A_TOT)
-          dma16(X, a_off[j] + (uint32_t)t * 128u, lds_addr(&act[st][0]) + (wave + W * j) * 1024);
+        if (witem + WI * j < A_TOT)
+          dma16(X, a_off[j] + (uint32_t)t * 128u, lds_addr(&act[slice][st][0]) + (witem + WI * j) * 1024);
     };
     // One step's MFMAs. A full pass (kFull: all RB row blocks present) has no
     // branches, so the conversions of one weight piece can overlap the MFMAs of
@@ -498,7 +514,7 @@ __global__ __launch_bounds__(W * kWave) void ffn_stream_shared_gu_kernel(
           for (int ks = 0; ks < 2; ++ks) {
             const int row = rb * 16 + li;
             const int chunk = ((WF::kActLane * lg + WF::kActSecond * ks) >> 3) ^ (row & 7);
-            xf[rb][ks] = *reinterpret_cast<const bf16x8*>(&act[st][row * 128 + chunk * 16]);
+            xf[rb][ks] = *reinterpret_cast<const bf16x8*>(&act[slice][st][row * 128 + chunk * 16]);
           }
         }
       }
@@ -541,11 +557,41 @@ __global__ __launch_bounds__(W * kWave) void ffn_stream_shared_gu_kernel(
     __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
     __builtin_amdgcn_s_barrier();
 
-    // ---- epilogue (as ffn_stream_kernel's gate/up pass)
+    if constexpr (KS > 1) {
+      // slices 1..KS-1 park their sums in the rings; slice 0 adds them in
+      // ascending slice order (nrb is the same for the whole workgroup)
+      f32x4* red = reinterpret_cast<f32x4*>(&act[0][0][0]);
+      auto red_at = [&](int sl, int rb, int ng, int m) {
+        return red + ((((sl - 1) * WI + witem) * RB + rb) * NG * NMAT + ng * NMAT + m) * kWave + lane;
+      };
+      if (slice > 0) {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+          if (rb < nrb)
+#pragma unroll
+            for (int ng = 0; ng < NG; ++ng)
+#pragma unroll
+              for (int m = 0; m < NMAT; ++m) *red_at(slice, rb, ng, m) = acc[rb][ng][m];
+      }
+      __syncthreads();
+      if (slice == 0) {
+        for (int sl = 1; sl < KS; ++sl)
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb)
+            if (rb < nrb)
+#pragma unroll
+              for (int ng = 0; ng < NG; ++ng)
+#pragma unroll
+                for (int m = 0; m < NMAT; ++m) acc[rb][ng][m] += *red_at(sl, rb, ng, m);
+      }
+      __syncthreads();   // the next pass's copies overwrite the rings
+    }
+
+    // ---- epilogue (as ffn_stream_kernel's gate/up pass), by slice 0
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       const int r = p0 + rb * 16 + li;
-      if (rb < nrb && r < nrows) {
+      if (slice == 0 && rb < nrb && r < nrows) {
         const long orow = (long)(row0 + r) * N;
 #pragma unroll
         for (int ng = 0; ng < NG; ++ng) {
@@ -782,33 +828,50 @@ hipError_t launch_stream_pass_rb(const FfnArgs& a, hipStream_t stream) {
   }
 }
 
-template <bool kScaleBf16, int F, int W>
+template <bool kScaleBf16, int F, int NG, int WI, int KS, int P>
 hipError_t launch_stream_shared_gu_w(const FfnArgs& a, hipStream_t stream) {
-  constexpr int NG = MOE_STREAM_NG_GU_WIDE;
   const int gpe = a.f / (16 * NG);
-  const dim3 grid((unsigned)((long)a.E * (gpe / W)));
-  hipLaunchKernelGGL((ffn_stream_shared_gu_kernel<kScaleBf16, F, NG, W, MOE_STREAM_P_SHARED>), grid,
-                     dim3(W * kWave), 0, stream, static_cast<const __bf16*>(a.x), a.sorted_slots, a.K, a.w_gate,
-                     a.w_up, a.s_gate, a.s_up, a.offsets, a.E, a.f, a.d, a.h);
+  const dim3 grid((unsigned)((long)a.E * (gpe / WI)));
+  hipLaunchKernelGGL((ffn_stream_shared_gu_kernel<kScaleBf16, F, NG, WI, KS, P>), grid,
+                     dim3(WI * KS * kWave), 0, stream, static_cast<const __bf16*>(a.x), a.sorted_slots, a.K,
+                     a.w_gate, a.w_up, a.s_gate, a.s_up, a.offsets, a.E, a.f, a.d, a.h);
   return hipGetLastError();
 }
 
-// Waves (items) per workgroup of the shared-activation gate/up pass: the most
-// of 4, 3, 2 that divides the items of an expert and still gives every CU a
-// workgroup; 2 always divides (f is a multiple of 64).
-int shared_gu_waves(int E, int f) {
+// Workgroup shape of the shared-activation gate/up pass.
+//   - Enough items for two 4-wave workgroups per CU: WI = 4 items, no split.
+//   - Else, with a third of an expert's items giving every CU a workgroup: WI = 3
+//     items with their reductions cut in two (KS = 2), six waves on the four
+//     SIMDs, where three unsplit items would leave one SIMD of every CU idle
+//     (the dense MLP layer: gate/up 90-96 -> 82-84 us).
+//   - Else the most of 4, 3, 2 items that divides an expert's items and still
+//     gives every CU a workgroup; 2 always divides (f is a multiple of 64).
+struct SharedGuShape {
+  int wi, ks;
+};
+SharedGuShape shared_gu_shape(int E, int f, int d) {
   const int gpe = f / (16 * MOE_STREAM_NG_GU_WIDE);
+  const long cus = MOE_STREAM_SHARED_MIN_WGS;
+  if (gpe % 4 == 0 && (long)E * (gpe / 4) >= 2 * cus) return {4, 1};
+  if (gpe % 3 == 0 && (long)E * (gpe / 3) >= cus && ((d >> 6) % 2) == 0) return {3, 2};
   for (int w = 4; w >= 2; --w)
-    if (gpe % w == 0 && (long)E * (gpe / w) >= MOE_STREAM_SHARED_MIN_WGS) return w;
-  return 2;
+    if (gpe % w == 0 && (long)E * (gpe / w) >= cus) return {w, 1};
+  return {2, 1};
 }
 
 template <bool kScaleBf16, int F>
 hipError_t launch_stream_shared_gu(const FfnArgs& a, hipStream_t stream) {
-  switch (shared_gu_waves(a.E, a.f)) {
-    case 4: return launch_stream_shared_gu_w<kScaleBf16, F, 4>(a, stream);
-    case 3: return launch_stream_shared_gu_w<kScaleBf16, F, 3>(a, stream);
-    default: return launch_stream_shared_gu_w<kScaleBf16, F, 2>(a, stream);
+  constexpr int NG = MOE_STREAM_NG_GU_WIDE;
+  SharedGuShape sh = shared_gu_shape(a.E, a.f, a.d);
+  if constexpr (WFormat<F>::kPieces == 1) {
+    if (sh.ks == 2) return launch_stream_shared_gu_w<kScaleBf16, F, NG, 3, 2, MOE_STREAM_P_SHARED_SPLIT>(a, stream);
+  } else if (sh.ks == 2) {
+    sh = {3, 1};   // bf16 weights: a split's ring of two-piece steps does not fit two waves per SIMD
+  }
+  switch (sh.wi) {
+    case 4: return launch_stream_shared_gu_w<kScaleBf16, F, NG, 4, 1, MOE_STREAM_P_SHARED>(a, stream);
+    case 3: return launch_stream_shared_gu_w<kScaleBf16, F, NG, 3, 1, MOE_STREAM_P_SHARED>(a, stream);
+    default: return launch_stream_shared_gu_w<kScaleBf16, F, NG, 2, 1, MOE_STREAM_P_SHARED>(a, stream);
   }
 }
 

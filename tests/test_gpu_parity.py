@@ -216,7 +216,9 @@ def test_combine_matches_oracle(T, d, K, act):
     (100, 128, 128, 16, 2, "bf16", "bf16", [0.0] * 5 + [100.0] + [0.0] * 10),  # hot expert 5 in every token
     (50, 128, 128, 64, 8, "bf16", "bf16", None),     # the largest E and K
     (300, 128, 2048, 16, 2, "bf16", "bf16", None),   # 37 rows per expert: shared-activation gate/up, 4 waves
-    (300, 128, 1536, 16, 2, "bf16", "bf16", None),   # the same with 3 waves per workgroup
+    (300, 128, 1536, 16, 2, "bf16", "bf16", None),   # the same with 3 items per workgroup, reductions cut in two
+    (600, 128, 1536, 16, 2, "bf16", "bf16", None),   # ... and more than 64 rows per expert: several passes
+    (300, 192, 1536, 16, 2, "bf16", "bf16", None),   # 3 items per workgroup, no cut (an odd number of steps)
     (5, 65536, 64, 2, 1, "bf16", "bf16", None),      # the largest d
     (3, 64, 131072, 2, 2, "bf16", "f32", None),      # the largest f
 ])
