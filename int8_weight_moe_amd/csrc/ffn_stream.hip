@@ -85,6 +85,18 @@ namespace {
 #ifndef MOE_STREAM_MIN_WAVES_WIDE
 #define MOE_STREAM_MIN_WAVES_WIDE 4096
 #endif
+// The gate/up pass of the 32-row variant splits its reductions (at most 4
+// ways) until it has MIN_WAVES_GU waves: shorter waves balance better at the
+// end of the pass. Measured (interleaved A/B): Mini decode, 14336 items split
+// in 2: 290-298 -> 277-290 us; the TP8 share of Large decode, 3072 items split
+// in 4: 142-154 -> 131-145 us; Large decode, 24576 items, stays unsplit (a
+// split of 2 measured 1-2% slower, 8 ways 10% slower on the TP8 share).
+#ifndef MOE_STREAM_MIN_WAVES_GU
+#define MOE_STREAM_MIN_WAVES_GU 16384
+#endif
+#ifndef MOE_STREAM_MAX_SPLIT_GU
+#define MOE_STREAM_MAX_SPLIT_GU 4
+#endif
 // activation prefetch ring of the 64-row variant (see the main loop)
 #ifndef MOE_STREAM_PA_WIDE
 #define MOE_STREAM_PA_WIDE 2
@@ -125,10 +137,11 @@ constexpr int ring_unroll(int a, int b) { return a / ring_gcd(a, b) * b; }
 
 // Reduction split (1, 2, 4 or 8) of a pass with `items` (expert, channel
 // group) items.
-int choose_split(long items, int RB) {
-  const long want = RB >= 4 ? MOE_STREAM_MIN_WAVES_WIDE : MOE_STREAM_MIN_WAVES;
+int choose_split(long items, int RB, bool gate_up = false) {
+  const long want = RB >= 4 ? MOE_STREAM_MIN_WAVES_WIDE : (gate_up ? MOE_STREAM_MIN_WAVES_GU : MOE_STREAM_MIN_WAVES);
+  const int max_ks = (gate_up && RB < 4) ? MOE_STREAM_MAX_SPLIT_GU : 8;
   int ks = 1;
-  while (ks < 8 && items * ks < want) ks *= 2;
+  while (ks < max_ks && items * ks < want) ks *= 2;
   return ks;
 }
 
@@ -820,7 +833,7 @@ hipError_t launch_stream_pass_rb(const FfnArgs& a, hipStream_t stream) {
                              : (RB >= 4 ? MOE_STREAM_NG_DN_WIDE : MOE_STREAM_NG_DN);
   const int N = kGateUp ? a.f : a.d;
   const long items = (long)a.E * (N / (16 * NG));
-  switch (choose_split(items, RB)) {
+  switch (choose_split(items, RB, kGateUp)) {
     case 1: return launch_stream_pass_ks<kGateUp, Act, kScaleBf16, F, RB, 1>(a, items, stream);
     case 2: return launch_stream_pass_ks<kGateUp, Act, kScaleBf16, F, RB, 2>(a, items, stream);
     case 4: return launch_stream_pass_ks<kGateUp, Act, kScaleBf16, F, RB, 4>(a, items, stream);
