@@ -21,11 +21,12 @@
 // has no idle waves for untouched experts. For at most 256 slots the gate/up
 // pass can take the expert ids instead of the permutation and write the
 // permutation itself (one launch fewer for a decode step).
-// With few experts (a dense MLP layer: one) there are too few items to keep
-// enough loads in flight, so the reduction axis of each item is cut into KS
-// slices streamed by the KS waves of one workgroup; the slices' fp32 partial
-// sums are added through LDS in ascending slice order before the epilogue, so
-// the result does not depend on scheduling and costs no extra HBM traffic.
+// With few items (a dense MLP layer has one expert) there are too few waves
+// to keep enough loads in flight, and long waves balance badly at the end of
+// the pass, so the reduction axis of each item is cut into KS slices streamed
+// by the KS waves of one workgroup; the slices' fp32 partial sums are added
+// through LDS in ascending slice order before the epilogue, so the result does
+// not depend on scheduling and costs no extra HBM traffic.
 // With more than 32 rows per expert every wave would re-read its rows'
 // activations from L2 at each step, so two variants share them through LDS
 // among the waves of a workgroup that work on neighbouring channel groups:
@@ -136,7 +137,8 @@ constexpr int ring_gcd(int a, int b) { return b == 0 ? a : ring_gcd(b, a % b); }
 constexpr int ring_unroll(int a, int b) { return a / ring_gcd(a, b) * b; }
 
 // Reduction split (1, 2, 4 or 8) of a pass with `items` (expert, channel
-// group) items.
+// group) items: the smallest that reaches the pass's wave target, within its
+// largest split.
 int choose_split(long items, int RB, bool gate_up = false) {
   const long want = RB >= 4 ? MOE_STREAM_MIN_WAVES_WIDE : (gate_up ? MOE_STREAM_MIN_WAVES_GU : MOE_STREAM_MIN_WAVES);
   const int max_ks = (gate_up && RB < 4) ? MOE_STREAM_MAX_SPLIT_GU : 8;
