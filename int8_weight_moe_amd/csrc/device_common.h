@@ -86,8 +86,12 @@ constexpr int waitcnt_vm_lgkm0(int vm) { return (vm & 15) | ((vm >> 4) << 14) | 
 //     is launched for the most row tiles the slot count allows, left the last
 //     XCD idle for the tiles that do not exist). The grid must hold
 //     xcds * per_xcd blocks.
-//   - Within a share, groups of GM row tiles take every channel tile before
-//     the next group, so a weight tile is read by GM row tiles in a row.
+//   - Each expert's row tiles form groups of at most GM (as even as
+//     possible; no group spans two experts), and a group takes every channel
+//     tile before the next group, so a weight tile is read by all the row
+//     tiles of its group in a row. (Groups of GM over all row tiles, which
+//     span expert boundaries and then read two experts' weights, measured
+//     1-1.5% slower on the Mini prefill passes.)
 // Returns false for blocks past the real tiles; else the expert, first row,
 // row count and channel tile.
 template <int BM, int GM>
@@ -114,16 +118,32 @@ __device__ __forceinline__ bool block_tile(const int32_t* __restrict__ offsets, 
   if (k >= per_xcd) return false;
   const int tile = (blockIdx.x % xcds) * per_xcd + k;
   if (tile >= total) return false;
-  const int group_tiles = GM * n_tiles_n;
-  const int group = tile / group_tiles;
-  const int in_group = tile - group * group_tiles;
-  const int gm = min(GM, m_tiles - group * GM);   // row tiles in this (possibly last) group
-  const int mt = group * GM + in_group % gm;
-  nt = in_group / gm;
-  const uint64_t hit = __ballot(lane < E && mt >= excl && mt < incl);
+  // the expert owning the tile (expert x owns tiles [excl_x, incl_x) * n_tiles),
+  // then the tile's balanced group of at most GM of that expert's row tiles:
+  // ceil(mt / GM) groups whose sizes differ by at most one, the larger first
+  const uint64_t hit = __ballot(lane < E && tile >= excl * n_tiles_n && tile < incl * n_tiles_n);
   const int x = __builtin_amdgcn_readfirstlane(__ffsll((unsigned long long)hit) - 1);
+  const int mt_e = __shfl(tiles, x);
+  const int local = tile - __shfl(excl, x) * n_tiles_n;
+  const int ngroups = (mt_e + GM - 1) / GM;
+  const int gbase = mt_e / ngroups, gextra = mt_e - gbase * ngroups;
+  const int big = (gbase + 1) * n_tiles_n;
+  int start_m, gm, in_group;
+  if (local < gextra * big) {
+    const int g = local / big;
+    gm = gbase + 1;
+    start_m = g * gm;
+    in_group = local - g * big;
+  } else {
+    const int l2 = local - gextra * big;
+    const int g2 = l2 / (gbase * n_tiles_n);
+    gm = gbase;
+    start_m = gextra * (gbase + 1) + g2 * gbase;
+    in_group = l2 - g2 * gbase * n_tiles_n;
+  }
+  nt = in_group / gm;
   e = x;
-  row0 = __builtin_amdgcn_readfirstlane(__shfl(o0, x) + (mt - __shfl(excl, x)) * BM);
+  row0 = __builtin_amdgcn_readfirstlane(__shfl(o0, x) + (start_m + in_group % gm) * BM);
   nrows = __builtin_amdgcn_readfirstlane(min(BM, __shfl(o1, x) - row0));
   return true;
 }

@@ -21,10 +21,10 @@
 // Waves are arranged WM x WN; a wave owns (BM/WM) x (BN/WN) outputs and issues
 // 16x16x32 bf16 MFMAs with the channels as MFMA rows and the tokens as MFMA
 // columns, so each lane ends with 4 consecutive channels of one row.
-// Tile order: row tiles are numbered expert by expert; tiles are visited in
-// groups of GM consecutive row tiles, channel tile by channel tile inside a
-// group, so the tiles that run together share GM activation tiles and a few
-// weight tiles. Workgroup ids are spread so that each XCD (workgroups are dealt
+// Tile order: row tiles are numbered expert by expert; each expert's row
+// tiles are visited in groups of at most GM, channel tile by channel tile
+// inside a group, so the tiles that run together share a few activation tiles
+// and weight tiles of one expert. Workgroup ids are spread so that each XCD (workgroups are dealt
 // round-robin to the 8 XCDs) runs a contiguous range of that order, an equal
 // share of the real tiles, and keeps its operands in its own L2.
 #include "device_common.h"
