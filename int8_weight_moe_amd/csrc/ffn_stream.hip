@@ -77,7 +77,7 @@ namespace {
 #ifndef MOE_STREAM_WAVES
 #define MOE_STREAM_WAVES 4
 #endif
-// Waves a pass wants in flight: the 32-row variant MIN_WAVES, the 64-row
+// Waves a pass wants in flight: the 32-row down pass MIN_WAVES, the 64-row
 // variant MIN_WAVES_WIDE (four times the MFMA and activation work per weight
 // byte, so more waves are needed to keep HBM busy).
 #ifndef MOE_STREAM_MIN_WAVES
