@@ -55,6 +55,12 @@ namespace {
 #ifndef MOE_STREAM_P_GU
 #define MOE_STREAM_P_GU 3
 #endif
+// ring of the unsplit 32-row gate/up pass, whose waves stream whole items
+// (Large decode: 5 stages 1009-1018 us against 3 stages 1031-1040 us; split
+// passes measured best with 2-3)
+#ifndef MOE_STREAM_P_GU_LONG
+#define MOE_STREAM_P_GU_LONG 5
+#endif
 #ifndef MOE_STREAM_NG_DN
 #define MOE_STREAM_NG_DN 4
 #endif
@@ -810,7 +816,7 @@ template <bool kGateUp, typename Act, bool kScaleBf16, int F, int RB, int KS>
 hipError_t launch_stream_pass_ks(const FfnArgs& a, long items, hipStream_t stream) {
   constexpr int NG = kGateUp ? (RB >= 4 ? MOE_STREAM_NG_GU_WIDE : MOE_STREAM_NG_GU)
                              : (RB >= 4 ? MOE_STREAM_NG_DN_WIDE : MOE_STREAM_NG_DN);
-  constexpr int P = kGateUp ? MOE_STREAM_P_GU : MOE_STREAM_P_DN;
+  constexpr int P = kGateUp ? ((KS == 1 && RB < 4) ? MOE_STREAM_P_GU_LONG : MOE_STREAM_P_GU) : MOE_STREAM_P_DN;
   const int N = kGateUp ? a.f : a.d;
   const int Kd = kGateUp ? a.d : a.f;
   const dim3 grid((unsigned)(KS > 1 ? items : (items + kStreamWaves - 1) / kStreamWaves));
