@@ -503,8 +503,12 @@ void ffn_tiled_dma_kernel(
     MOE_DMA_COMPUTE(AC, BC, MBV)                                                            \
   }
   // A partial row tile (the last one of an expert) skips the MFMAs and the
-  // fragment reads of the 16-row blocks it does not have, in this wave's rows.
+  // fragment reads of the 16-row blocks it does not have, in this wave's rows;
+  // each count of blocks has its own copy of the loop, free of branches
+  // (against one copy with a runtime count: Mini prefill gate/up and down
+  // about 1% faster).
   const int mb_valid = min(MB, max(0, (nrows - wm * TM + 15) / 16));
+  static_assert(MB <= 8, "one loop copy per row-block count, up to 8");
 #define MOE_DMA_MAIN_LOOP(MBV)                                                              \
   {                                                                                         \
     int k0 = 0;                                                                             \
@@ -527,10 +531,20 @@ void ffn_tiled_dma_kernel(
       if (k0 < nk) MOE_DMA_STEP(k0, As0, Bs0, As1, Bs1, MBV)                                \
     }                                                                                       \
   }
-  if (mb_valid == MB) {
-    MOE_DMA_MAIN_LOOP(MB)
-  } else {
-    MOE_DMA_MAIN_LOOP(mb_valid)
+  auto main_loop = [&](auto mbc) {
+    constexpr int MBV = decltype(mbc)::value;
+    MOE_DMA_MAIN_LOOP(MBV)
+  };
+  switch (mb_valid) {
+    case 0: main_loop(int_constant<0>{}); break;
+    case 1: main_loop(int_constant<(1 < MB ? 1 : MB)>{}); break;
+    case 2: main_loop(int_constant<(2 < MB ? 2 : MB)>{}); break;
+    case 3: main_loop(int_constant<(3 < MB ? 3 : MB)>{}); break;
+    case 4: main_loop(int_constant<(4 < MB ? 4 : MB)>{}); break;
+    case 5: main_loop(int_constant<(5 < MB ? 5 : MB)>{}); break;
+    case 6: main_loop(int_constant<(6 < MB ? 6 : MB)>{}); break;
+    case 7: main_loop(int_constant<(7 < MB ? 7 : MB)>{}); break;
+    default: main_loop(int_constant<MB>{}); break;
   }
 #undef MOE_DMA_MAIN_LOOP
 #undef MOE_DMA_STEP
