@@ -71,6 +71,15 @@ long tiled_grid_blocks(bool gate_up, long m_tiles_max, int n_tiles_n) {
 #ifndef MOE_TILE_GM
 #define MOE_TILE_GM 4
 #endif
+// row tiles per group of the direct-to-LDS gate/up pass: its weight tiles
+// (two matrices) are the larger operand, so larger groups read them fewer
+// times (Mini prefill gate/up, interleaved A/B on one box: groups of 8
+// 3321-3333 us, of 6 3361-3369, of 4 3434-3466; on another 3336-3341 against
+// 3444-3512; dense MLP prefill 0.5-1.5% faster, Large skewed within 0.5%);
+// the down pass keeps 4 (8 measured 2% slower on Large skewed)
+#ifndef MOE_TILE_GM_GU
+#define MOE_TILE_GM_GU 8
+#endif
 // bf16 activations use the direct-to-LDS kernel below (1) or the register-staged one (0)
 #ifndef MOE_TILE_DMA
 #define MOE_TILE_DMA 1
@@ -587,7 +596,7 @@ void ffn_tiled_dma_kernel(
 
 template <bool kGateUp, bool kScaleBf16, int F, int DBN>
 hipError_t launch_dma_pass(const FfnArgs& a, hipStream_t stream) {
-  constexpr int GM = MOE_TILE_GM;
+  constexpr int GM = kGateUp ? MOE_TILE_GM_GU : MOE_TILE_GM;
   constexpr int DBM = MOE_DMA_BM, DWM = MOE_DMA_WM, DWN = MOE_DMA_WN, DST = MOE_DMA_STAGES;
   constexpr int DCH = kGateUp ? DBN / 2 : DBN;
   const int N = kGateUp ? a.f : a.d;
