@@ -86,15 +86,16 @@ constexpr int waitcnt_vm_lgkm0(int vm) { return (vm & 15) | ((vm >> 4) << 14) | 
 //     is launched for the most row tiles the slot count allows, left the last
 //     XCD idle for the tiles that do not exist). The grid must hold
 //     xcds * per_xcd blocks.
-//   - Each expert's row tiles form groups of at most GM (as even as
-//     possible; no group spans two experts), and a group takes every channel
+//   - Each expert's row tiles form groups of at most GM (GM_LONG for an
+//     expert with at least 3*GM row tiles; as even as possible; no group spans
+//     two experts), and a group takes every channel
 //     tile before the next group, so a weight tile is read by all the row
 //     tiles of its group in a row. (Groups of GM over all row tiles, which
 //     span expert boundaries and then read two experts' weights, measured
 //     1-1.5% slower on the Mini prefill passes.)
 // Returns false for blocks past the real tiles; else the expert, first row,
 // row count and channel tile.
-template <int BM, int GM>
+template <int BM, int GM, int GM_LONG = GM>
 __device__ __forceinline__ bool block_tile(const int32_t* __restrict__ offsets, int E, int n_tiles_n, int xcds,
                                            int grain, int& e, int& row0, int& nrows, int& nt) {
   const int lane = threadIdx.x & (kWave - 1);
@@ -125,7 +126,8 @@ __device__ __forceinline__ bool block_tile(const int32_t* __restrict__ offsets, 
   const int x = __builtin_amdgcn_readfirstlane(__ffsll((unsigned long long)hit) - 1);
   const int mt_e = __shfl(tiles, x);
   const int local = tile - __shfl(excl, x) * n_tiles_n;
-  const int ngroups = (mt_e + GM - 1) / GM;
+  const int gmax = (mt_e >= 3 * GM) ? GM_LONG : GM;   // experts with many row tiles: larger groups
+  const int ngroups = (mt_e + gmax - 1) / gmax;
   const int gbase = mt_e / ngroups, gextra = mt_e - gbase * ngroups;
   const int big = (gbase + 1) * n_tiles_n;
   int start_m, gm, in_group;

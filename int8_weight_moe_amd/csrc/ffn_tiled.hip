@@ -76,7 +76,9 @@ long tiled_grid_blocks(bool gate_up, long m_tiles_max, int n_tiles_n) {
 // times (Mini prefill gate/up, interleaved A/B on one box: groups of 8
 // 3321-3333 us, of 6 3361-3369, of 4 3434-3466; on another 3336-3341 against
 // 3444-3512; dense MLP prefill 0.5-1.5% faster, Large skewed within 0.5%);
-// the down pass keeps 4 (8 measured 2% slower on Large skewed)
+// the down pass keeps 4 (8 measured 2% slower on Large skewed). An expert with
+// at least 3*8 row tiles takes gate/up groups of up to 16 (Large skewed's two
+// hot experts, 52 row tiles: gate/up 0.5-1% faster, its TP8 share 0.7%)
 #ifndef MOE_TILE_GM_GU
 #define MOE_TILE_GM_GU 8
 #endif
@@ -373,7 +375,9 @@ void ffn_tiled_dma_kernel(
   const int lg = lane >> 4;
 
   int e, row0, nrows, nt;
-  if (!block_tile<BM, GM>(offsets, E, n_tiles_n, kXcds, xcd_grain(kGateUp, n_tiles_n), e, row0, nrows, nt)) return;
+  constexpr int GM_LONG = kGateUp ? 2 * GM : GM;
+  if (!block_tile<BM, GM, GM_LONG>(offsets, E, n_tiles_n, kXcds, xcd_grain(kGateUp, n_tiles_n), e, row0, nrows, nt))
+    return;
   const int n0 = nt * CH_TILE;
 
   // activation sources: instruction j of this wave covers rows 8*(A_INSTR*wave + j) + lane/8;
