@@ -6,14 +6,17 @@ gate/up contraction with SwiGLU, down contraction, weighted combine) over one
 batch of synthetic tokens, through the fused C-ABI call moe_forward. Inputs
 and int8 weights are resident in HBM before timing starts.
 
-Default workload: Jamba-Mini-shaped decode step, T=32 tokens, d=4096,
-f=14336, 16 experts, top-2, bf16 activations, int8 per-output-channel weights
-with bf16 scales. The prefill workload that shares the same weights (T=8192)
-is measured in the same run and reported under "prefill".
+Default (headline) workload: the Jamba-1.5-Large-shaped MoE layer at prefill
+with skewed routing, T=16384 tokens, d=8192, f=24576, 16 experts, top-2,
+bf16 activations, int8 per-output-channel weights with bf16 scales, router
+bias +2.0 on experts 0 and 1 (the largest workload that fits one GPU). The
+decode workload on the same weights (T=64) is measured in the same run and
+reported under "decode".
 
-Printed: one JSON line with the throughput (tokens/s), the roofline of the
-dominant kernel measured with HIP events on the launch stream, and the CPU
-oracle timed on a bounded sample of the same workload (host cores).
+Printed: one JSON line with the throughput (tokens/s), the step-time spread,
+the roofline of the dominant kernel measured with HIP events on the launch
+stream, and the CPU oracle timed on a bounded sample of the same workload
+(host cores).
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--gpus 1]
 """
@@ -34,23 +37,26 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0       # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 
-# decode workload -> the prefill workload with the same weights
-SIBLING = {"mini-decode": "mini-prefill", "large-decode": "large-prefill-skewed",
-           "large-mlp-decode": "large-mlp-prefill", "large-decode-tp8": "large-prefill-skewed-tp8"}
+# decode and prefill workloads that share one layer's weights
+_PAIRS = {"mini-decode": "mini-prefill", "large-decode": "large-prefill-skewed",
+          "large-mlp-decode": "large-mlp-prefill", "large-decode-tp8": "large-prefill-skewed-tp8"}
+SIBLING = {**_PAIRS, **{v: k for k, v in _PAIRS.items()}}
+HEADLINE = "large-prefill-skewed"
 
 
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="mini-decode")
-    ap.add_argument("--prefill-steps", type=int, default=10)
-    ap.add_argument("--no-prefill", action="store_true", help="skip the sibling prefill workload")
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--sibling-steps", type=int, default=50,
+                    help="timed steps of the sibling workload on the same weights (decode: 50, prefill: 10)")
+    ap.add_argument("--no-sibling", action="store_true", help="skip the sibling workload on the same weights")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-compare", action="store_true",
                     help="skip the weight-encoding comparators (the same layer with bf16 or fp8 weights)")
-    ap.add_argument("--cpu-sample-experts", type=int, default=4)
+    ap.add_argument("--no-vendor", action="store_true", help="skip the vendor bf16 GEMM context figures")
     ap.add_argument("--path", choices=["auto", "stream", "tiled"], default="auto")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (reference for HBM byte counters)")
@@ -119,7 +125,11 @@ def ffn_path_used(w, path):
 
 # ----------------------------------------------------------------------------- timing
 def time_forward(layer, x, path, steps, warmup, dense=False):
-    """Average step time of the fused call: moe_forward, or moe_mlp_forward for a dense MLP layer."""
+    """Step time of the fused call: moe_forward, or moe_mlp_forward for a dense MLP layer.
+
+    One timed region of `steps` back-to-back calls bracketed by synchronisations;
+    a HIP event after every call also gives each step's own duration. Returns
+    (ms per step over the region, wall ms per step, [per-step ms])."""
     import torch
     from int8_weight_moe_amd import moe_mlp_forward
     y = torch.empty_like(x)
@@ -136,15 +146,28 @@ def time_forward(layer, x, path, steps, warmup, dense=False):
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     t0 = time.perf_counter()
-    start.record()
-    for _ in range(steps):
+    evs[0].record()
+    for i in range(steps):
         step()
-    end.record()
+        evs[i + 1].record()
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) * 1e3 / steps
-    return start.elapsed_time(end) / steps, wall
+    per_step = [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
+    return evs[0].elapsed_time(evs[steps]) / steps, wall, per_step
+
+
+def spread(per_step):
+    """p10 / median / p90 of the per-step durations (ms)."""
+    v = sorted(per_step)
+
+    def q(p):
+        k = (len(v) - 1) * p
+        lo = int(k)
+        hi = min(lo + 1, len(v) - 1)
+        return v[lo] + (v[hi] - v[lo]) * (k - lo)
+    return {"p10_ms": round(q(0.1), 4), "p50_ms": round(q(0.5), 4), "p90_ms": round(q(0.9), 4)}
 
 
 def time_stages(layer, x, path, steps, warmup, dense=False):
@@ -253,53 +276,74 @@ def roofline(w, alg, stages, dominant, workload, hbm_bound):
 
 
 # ----------------------------------------------------------------------------- CPU oracle baseline
-def cpu_baseline(w, x_host, layer, src, n_experts):
-    """The oracle (unchanged) on the host cores, on a bounded sample of the step.
+def cpu_baseline(w, x_host, layer, src, experts_sampled=(0, 15), rows_fit=(32, 160)):
+    """The oracle (unchanged, fp64 NumPy) on the host cores, on a bounded sample of the step.
 
-    Timed: the router + gate for every token, the SwiGLU experts of `n_experts`
-    touched experts (all their rows) and the combine of those rows. The step
-    estimate scales the expert time by touched / sampled experts.
+    Timed in full: the router + top-K gate over all T tokens. Timed on a
+    sample: the SwiGLU expert FFN plus the combine of a few experts at two row
+    counts each (the first rows of each sampled expert's segment). The oracle's
+    cost of one expert over n rows is a + b*n (a: its per-call conversion of the
+    expert's int8 weights to fp64; b: the three contractions per row, linear in
+    n), all experts having the same shape; a and b come from a least-squares
+    fit over the sampled calls, and the step estimate is
+        route(T) + sum over touched experts e of (a + b * rows_e).
+    BLAS threads are pinned to the cores this process may run on.
     """
     import numpy as np
-    import torch
     from oracle import moe as omoe
     from oracle import quant as oquant
+    cores = len(os.sched_getaffinity(0))
     try:
-        import threadpoolctl
-        cores = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()) or 1
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(limits=cores)
     except Exception:  # pragma: no cover
-        cores = len(os.sched_getaffinity(0))
-
-    x64 = x_host.double().numpy()
-    wr64 = layer.router_w.double().cpu().numpy()
-    b64 = None if layer.bias is None else layer.bias.double().cpu().numpy()
-    ids, gw, _ = omoe.route(x64, wr64, b64, w.K)
-    touched = sorted(set(ids.reshape(-1).tolist()))
-    sample = touched[:n_experts]
-    W = {k: {} for k in ("q_gate", "s_gate", "q_up", "s_up", "q_down", "s_down")}
-    for e in sample:   # load-time quantization by the oracle: not timed
-        for k in ("gate", "up", "down"):
-            q, s = oquant.quantize_rows(src["w_" + k][e].double().cpu().numpy(), w.scale)
-            W["q_" + k][e], W["s_" + k][e] = q, s
-    times = []
-    for _ in range(3):
-        t0 = time.perf_counter()
-        ids2, gw2, _ = omoe.route(x64, wr64, b64, w.K)
-        t1 = time.perf_counter()
-        o = omoe.expert_outputs(x64, ids2, W, experts=sample)
-        mask = np.isin(ids2, sample)
-        y = omoe.combine(np.where(mask[..., None], o, 0.0), np.where(mask, gw2, 0.0))
-        t2 = time.perf_counter()
-        times.append((t1 - t0, t2 - t1))
-    tr = statistics.median(t[0] for t in times)
-    te = statistics.median(t[1] for t in times)
-    est = tr + te * len(touched) / len(sample)
-    del y
+        limiter = None
+    try:
+        x64 = x_host.double().numpy()
+        wr64 = layer.router_w.double().cpu().numpy()
+        b64 = None if layer.bias is None else layer.bias.double().cpu().numpy()
+        t_route = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            ids, gw, _ = omoe.route(x64, wr64, b64, w.K)
+            t_route.append(time.perf_counter() - t0)
+        tr = statistics.median(t_route)
+        flat = ids.reshape(-1)
+        counts = np.bincount(flat, minlength=w.E)
+        sample = [e for e in experts_sampled if e < w.E and counts[e] > 0]
+        pts = []   # (rows, seconds)
+        for e in sample:
+            W = {}
+            for k in ("gate", "up", "down"):   # load-time quantization by the oracle: not timed
+                q, sc = oquant.quantize_rows(src["w_" + k][e].double().cpu().numpy(), w.scale)
+                W["q_" + k], W["s_" + k] = {e: q}, {e: sc}
+            tt, kk = np.nonzero(ids == e)      # the expert's slots in sorted (slot) order
+            for n in rows_fit:
+                n = min(n, tt.size)
+                sel = np.full_like(ids, -1)
+                sel[tt[:n], kk[:n]] = e
+                t0 = time.perf_counter()
+                o = omoe.expert_outputs(x64, sel, W, experts=[e])
+                m = sel >= 0
+                omoe.combine(np.where(m[..., None], o, 0.0), np.where(m, gw, 0.0))
+                pts.append((n, time.perf_counter() - t0))
+            del W
+        A = np.array([[1.0, n] for n, _ in pts])
+        a_fit, b_fit = np.linalg.lstsq(A, np.array([t for _, t in pts]), rcond=None)[0]
+        touched = counts[counts > 0]
+        est = tr + len(touched) * a_fit + b_fit * float(touched.sum())
+    finally:
+        if limiter is not None:
+            limiter.unregister()
+    flops = 6.0 * w.T * w.K * w.d * w.f + 2.0 * w.T * w.d * w.E
     return {"value": round(w.T / est, 2), "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"router+gate over all {w.T} tokens; SwiGLU experts + combine for {len(sample)} of "
-                      f"{len(touched)} touched experts (all their rows), fp64 NumPy; step time scaled by "
-                      f"{len(touched)}/{len(sample)}; median of 3",
-            "step_ms_estimate": round(est * 1e3, 1)}
+            "dtype": "f64",
+            "sample": (f"router+gate over all {w.T} tokens timed in full (median of 3); SwiGLU expert FFN + combine "
+                       f"of experts {sample} timed on the first {list(rows_fit)} rows of each segment; per-expert "
+                       f"cost fit as a + b*rows (a = {a_fit * 1e3:.1f} ms, b = {b_fit * 1e3:.3f} ms/row) and summed "
+                       f"over the {len(touched)} touched experts' {int(touched.sum())} rows"),
+            "step_ms_estimate": round(est * 1e3, 1), "route_ms": round(tr * 1e3, 1),
+            "gflops": round(flops / est / 1e9, 1)}
 
 
 def vendor_gemm_reference(wp, dev, iters=10):
@@ -327,30 +371,46 @@ def vendor_gemm_reference(wp, dev, iters=10):
     return out
 
 
-def measure_prefill(layer, wp, xp, bias, args, dense, wfmt="int8"):
-    """Step time, kernel split and roofline of the sibling prefill workload on this layer."""
-    from int8_weight_moe_amd._lib import MOE_PATH_AUTO
+def measure(layer, wl, x, bias, steps, warmup, dense, path, wfmt="int8"):
+    """Step time, spread, kernel split, layer rates and dominant-kernel roofline of one workload."""
     orig_bias = layer.bias
-    if bias is not None:
-        layer.bias = bias
-    cp = touched_rows(layer, xp, MOE_PATH_AUTO)
-    ap_ = algorithmic(wp, cp, wfmt)
-    pms, _ = time_forward(layer, xp, MOE_PATH_AUTO, args.prefill_steps, 2, dense)
-    pst = time_stages(layer, xp, MOE_PATH_AUTO, max(3, args.prefill_steps // 2), 1, dense)
-    layer.bias = orig_bias
-    pdom = max(("gate_up", "down"), key=lambda k: pst[k])
-    log(f"prefill {wp.name} ({wfmt} weights): {pms:.3f} ms/step; stages (us): "
-        + ", ".join(f"{k}={v:.1f}" for k, v in pst.items()))
-    out = {
-        "workload": wp.name, "T": wp.T, "ms_per_step": round(pms, 4),
-        "tokens_per_s": round(wp.T / (pms * 1e-3), 1),
-        "layer_tflops": round(ap_["layer_flops"] / (pms * 1e-3) / 1e12, 1),
-        "layer_mfma_frac": round(ap_["layer_flops"] / (pms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
-        "kernels_us": {k: round(v, 2) for k, v in pst.items()},
-    }
+    layer.bias = bias
+    try:
+        counts = touched_rows(layer, x, path)
+        alg = algorithmic(wl, counts, wfmt)
+        ms, wall_ms, per_step = time_forward(layer, x, path, steps, warmup, dense)
+        stages = time_stages(layer, x, path, max(3, steps // 2) if wl.T * wl.K > 64 * wl.E else steps,
+                             max(1, warmup // 2), dense)
+    finally:
+        layer.bias = orig_bias
+    used = ffn_path_used(wl, path)
+    dom = max(("gate_up", "down"), key=lambda k: stages[k])
+    s = ms * 1e-3
+    out = {"workload": wl.name, "T": wl.T, "ffn_path": used, "steps": steps, "ms_per_step": round(ms, 4),
+           "wall_ms_per_step": round(wall_ms, 4), **spread(per_step),
+           "tokens_per_s": round(wl.T / s, 1),
+           "layer": {"algorithmic_GB": round(alg["layer_bytes"] / 1e9, 4),
+                     "hbm_GBps": round(alg["layer_bytes"] / s / 1e9, 1),
+                     "hbm_frac": round(alg["layer_bytes"] / s / 1e9 / HBM_PEAK_GBPS, 4),
+                     "tflops": round(alg["layer_flops"] / s / 1e12, 2),
+                     "mfma_frac": round(alg["layer_flops"] / s / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "touched_experts": alg["touched"]},
+           "kernels_us": {k: round(v, 2) for k, v in stages.items()}}
     if wfmt == "int8":
-        out["roofline"] = roofline(wp, ap_, pst, pdom, wp.name, ffn_path_used(wp, MOE_PATH_AUTO) == "stream")
+        out["roofline"] = roofline(wl, alg, stages, dom, wl.name, used == "stream")
+        if used == "stream" and wl.T * wl.K <= 256 and not dense:
+            out["roofline"]["note"] = ("timed as the staged moe_expert_gate_up call, which reads the permutation; "
+                                       "inside moe_forward the same pass derives it from the routing ids")
+    log(f"{wl.name} ({wfmt} weights): {ms:.4f} ms/step (p10 {out['p10_ms']}, p90 {out['p90_ms']}); stages (us): "
+        + ", ".join(f"{k}={v:.1f}" for k, v in stages.items()))
     return out
+
+
+def workload_bias(wl, dev):
+    import torch
+    if not wl.has_bias:
+        return None
+    return torch.tensor([wl.hot_bias, wl.hot_bias] + [0.0] * (wl.E - 2), device=dev)
 
 
 # ----------------------------------------------------------------------------- main
@@ -373,25 +433,17 @@ def main():
     log(f"weights drawn and quantized on the GPU ({qms:.1f} ms for {3 * w.E * w.d * w.f / 1e9:.2f} G weights)")
     x_host = workloads.draw_activations(w)
     x = x_host.to(dev)
-    counts = touched_rows(layer, x, path)
-    alg = algorithmic(w, counts)
+    bias = workload_bias(w, dev)
 
-    ms, wall_ms = time_forward(layer, x, path, args.steps, args.warmup, dense)
-    log(f"forward: {ms * 1e3:.1f} us/step (wall {wall_ms * 1e3:.1f} us)")
-    stages = time_stages(layer, x, path, args.steps, args.warmup, dense)
-    log("stages (us): " + ", ".join(f"{k}={v:.1f}" for k, v in stages.items()))
-    dominant = max(("gate_up", "down"), key=lambda k: stages[k])
-    used_path = ffn_path_used(w, path)
-
-    layer_s = ms * 1e-3
+    head = measure(layer, w, x, bias, args.steps, args.warmup, dense, path)
     result = {
         "metric": "MLP-layer tokens/s" if dense else "MoE-layer tokens/s",
-        "value": round(w.T / layer_s, 1),
+        "value": head["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms, 4),
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -399,29 +451,32 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "T": w.T, "d": w.d, "f": w.f, "E": w.E, "K": w.K,
                    "weights": f"int8 per-output-channel, {w.scale} scales", "activations": w.act,
-                   "ffn_path": used_path, "parallelism": "single GPU"},
-        "roofline": roofline(w, alg, stages, dominant, w.name, used_path == "stream"),
-        "layer": {"algorithmic_GB": round(alg["layer_bytes"] / 1e9, 4),
-                  "hbm_GBps": round(alg["layer_bytes"] / layer_s / 1e9, 1),
-                  "hbm_frac": round(alg["layer_bytes"] / layer_s / 1e9 / HBM_PEAK_GBPS, 4),
-                  "tflops": round(alg["layer_flops"] / layer_s / 1e12, 2),
-                  "touched_experts": alg["touched"]},
-        "kernels_us": {k: round(v, 2) for k, v in stages.items()},
+                   "router_bias": f"+{w.hot_bias} on experts 0 and 1" if w.has_bias else "none",
+                   "ffn_path": head["ffn_path"], "parallelism": "single GPU"},
+        "roofline": head["roofline"],
+        "spread": {k: head[k] for k in ("p10_ms", "p50_ms", "p90_ms")},
+        "wall_ms_per_step": head["wall_ms_per_step"],
+        "layer": head["layer"],
+        "kernels_us": head["kernels_us"],
         "quantize_ms": round(qms, 2),
     }
 
-    # the sibling prefill workload of the same layer (same weights)
-    prefill_x, prefill_bias = None, None
-    sib = SIBLING.get(w.name)
-    if sib and not args.no_prefill:
-        wp = workloads.ALL_WORKLOADS[sib]
-        if (wp.d, wp.f, wp.E) == (w.d, w.f, w.E):
-            prefill_x = workloads.draw_activations(wp).to(dev)
-            if wp.has_bias:
-                prefill_bias = torch.tensor([wp.hot_bias, wp.hot_bias] + [0.0] * (w.E - 2), device=dev)
-            result["prefill"] = measure_prefill(layer, wp, prefill_x, prefill_bias, args, dense)
-            result["prefill"]["vendor_bf16_gemm"] = vendor_gemm_reference(wp, dev)
-            log(f"vendor bf16 GEMM reference (hipBLASLt, ungrouped): {result['prefill']['vendor_bf16_gemm']}")
+    # the sibling workload on the same weights (decode next to prefill, or the reverse)
+    sib_x, sib_bias, sib = None, None, SIBLING.get(w.name)
+    if sib and not args.no_sibling:
+        ws_ = workloads.ALL_WORKLOADS[sib]
+        if (ws_.d, ws_.f, ws_.E) == (w.d, w.f, w.E):
+            sib_x = workloads.draw_activations(ws_).to(dev)
+            sib_bias = workload_bias(ws_, dev)
+            key = "decode" if ws_.T * ws_.K <= 64 * ws_.E else "prefill"
+            steps = args.sibling_steps if key == "decode" else max(5, args.sibling_steps // 5)
+            result[key] = measure(layer, ws_, sib_x, sib_bias, steps, max(2, args.warmup), dense, MOE_PATH_AUTO)
+
+    if not args.no_vendor:
+        wp = w if w.T * w.K > 64 * w.E else (workloads.ALL_WORKLOADS[sib] if sib else None)
+        if wp is not None and wp.T * wp.K > 64 * wp.E:
+            result["vendor_bf16_gemm"] = {"workload": wp.name, **vendor_gemm_reference(wp, dev)}
+            log(f"vendor bf16 GEMM reference (hipBLASLt, ungrouped): {result['vendor_bf16_gemm']}")
 
     # weight-encoding comparators: the same layer, inputs and schedule choice
     if not args.no_compare and w.act == "bf16" and w.weight_src == "bf16":
@@ -433,29 +488,26 @@ def main():
             else:
                 ex = quantize_experts_fp8(src["w_gate"], src["w_up"], src["w_down"], workloads.TORCH_DTYPE[w.scale])
             clayer = MoeLayer(layer.router_w, layer.bias, ex, w.K)
-            cms, _ = time_forward(clayer, x, path, args.steps, args.warmup, dense)
-            cst = time_stages(clayer, x, path, args.steps, args.warmup, dense)
-            calg = algorithmic(w, counts, wfmt=name)
-            log(f"{name} weights: {cms * 1e3:.1f} us/step; stages (us): "
-                + ", ".join(f"{k}={v:.1f}" for k, v in cst.items()))
             entry = {"weights": "bf16 as stored, no scales" if name == "bf16" else
-                     f"fp8 e4m3 per-output-channel, {w.scale} scales",
-                     "ms_per_step": round(cms, 4), "tokens_per_s": round(w.T / (cms * 1e-3), 1),
-                     "int8_speedup": round(cms / ms, 3),
-                     "layer_GB": round(calg["layer_bytes"] / 1e9, 4),
-                     "hbm_GBps": round(calg["layer_bytes"] / (cms * 1e-3) / 1e9, 1),
-                     "kernels_us": {k: round(v, 2) for k, v in cst.items()}}
-            if prefill_x is not None:
-                wp = workloads.ALL_WORKLOADS[sib]
-                pr = measure_prefill(clayer, wp, prefill_x, prefill_bias, args, dense, wfmt=name)
-                entry["prefill"] = {"workload": wp.name, "ms_per_step": pr["ms_per_step"],
-                                    "int8_speedup": round(pr["ms_per_step"] / result["prefill"]["ms_per_step"], 3),
-                                    "kernels_us": pr["kernels_us"]}
+                     f"fp8 e4m3 per-output-channel, {w.scale} scales"}
+            c = measure(clayer, w, x, bias, args.steps, args.warmup, dense, path, wfmt=name)
+            entry[w.name] = {"ms_per_step": c["ms_per_step"], "int8_speedup": round(c["ms_per_step"] / head["ms_per_step"], 3),
+                             "layer_GBps": c["layer"]["hbm_GBps"], "layer_tflops": c["layer"]["tflops"],
+                             "kernels_us": c["kernels_us"]}
+            if sib_x is not None and not args.no_sibling:
+                ws_ = workloads.ALL_WORKLOADS[sib]
+                key = "decode" if ws_.T * ws_.K <= 64 * ws_.E else "prefill"
+                steps = args.sibling_steps if key == "decode" else max(5, args.sibling_steps // 5)
+                c2 = measure(clayer, ws_, sib_x, sib_bias, steps, max(2, args.warmup), dense, MOE_PATH_AUTO, wfmt=name)
+                entry[ws_.name] = {"ms_per_step": c2["ms_per_step"],
+                                   "int8_speedup": round(c2["ms_per_step"] / result[key]["ms_per_step"], 3),
+                                   "layer_GBps": c2["layer"]["hbm_GBps"], "layer_tflops": c2["layer"]["tflops"],
+                                   "kernels_us": c2["kernels_us"]}
             comp[name + "_weights"] = entry
             del ex, clayer
             torch.cuda.empty_cache()
         result["comparators"] = comp
-    del prefill_x
+    del sib_x
 
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib << 20
@@ -467,9 +519,10 @@ def main():
         log(f"copy calibration: 3 x {args.copy_calibration_mib} MiB device copies")
         del a, b
 
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not dense:
         log("timing the CPU oracle on a bounded sample ...")
-        result["cpu_baseline"] = cpu_baseline(w, x_host, layer, src, args.cpu_sample_experts)
+        result["cpu_baseline"] = cpu_baseline(w, x_host, layer, src)
+        log(f"cpu baseline: {result['cpu_baseline']}")
     print(json.dumps(result), flush=True)
 
 

@@ -140,6 +140,9 @@ moe_status moe_route(const moe_shape* shape, const void* x, const void* router_w
                      hipStream_t stream);
 
 /* Group the T*K slots by expert (stable: ascending slot inside an expert).
+ * Source: Jamba-1.5 paper, "Model Architecture": each token is sent to the
+ * top K of n experts, so every expert sees its own subset of the tokens; this
+ * call gathers each expert's slots into one contiguous segment.
  *   topk_ids       [T*K] int32 in, values in [0, E)
  *   expert_offsets [E+1] int32 out: expert e owns sorted rows [off[e], off[e+1])
  *   sorted_slots   [T*K] int32 out: slot held by each sorted row
@@ -151,6 +154,9 @@ moe_status moe_permute(const moe_shape* shape, const int32_t* topk_ids,
                        int32_t* slot_to_row, hipStream_t stream);
 
 /* Expert SwiGLU FFNs on the permuted rows (the ExpertsInt8 contraction).
+ * Source: Jamba-1.5 paper, "Serving Considerations and Improvements": the
+ * expert weights stay INT8 in memory and become BF16 values inside the fused
+ * MoE kernel, right before the contraction; activations stay BF16.
  *   x              [T, d] act_dtype (row of sorted row r is token sorted_slots[r] / K)
  *   expert_offsets [E+1], sorted_slots [T*K] from moe_permute
  *   w_gate, w_up   [E, f, d];  w_down [E, d, f] -- shape->weight_fmt encoding, tiled layout (moe_pack_rows)
@@ -165,7 +171,9 @@ moe_status moe_expert_ffn(const moe_shape* shape, const void* x,
                           float* y_rows, void* workspace, size_t workspace_bytes,
                           hipStream_t stream);
 
-/* The two passes of moe_expert_ffn, callable on their own (same kernels):
+/* The two passes of moe_expert_ffn, callable on their own (same kernels;
+ * source as moe_expert_ffn: Jamba-1.5 paper, "Serving Considerations and
+ * Improvements"):
  * gate/up  h[r] = silu(s_g * (q_g . x_r)) * (s_u * (q_u . x_r))  for every sorted row r,
  *          h [T*K, f] bf16 out (rows past off[E] untouched);
  * down     y_rows[r] = s_d * (q_d . h[r]),  h [T*K, f] bf16 in, y_rows [T*K, d] fp32 out.
@@ -185,12 +193,19 @@ moe_status moe_expert_down(const moe_shape* shape, const void* h, const int32_t*
                            size_t workspace_bytes, hipStream_t stream);
 
 /* Weighted combine back to token order: y[t] = sum_k topk_w[t,k] * y_rows[slot_to_row[t*K+k]]
+ * Source: Jamba-1.5 paper, "Model Architecture": the MoE module takes the
+ * place of the MLP, so its output is the gate-weighted sum of the K chosen
+ * experts' outputs, one [d] vector per token.
  * (k ascending, fp32, no atomics); a slot with row -1 contributes nothing.
  *   y [T, d] act_dtype out. */
 moe_status moe_combine(const moe_shape* shape, const float* y_rows, const int32_t* slot_to_row,
                        const float* topk_w, void* y, hipStream_t stream);
 
 /* The whole layer: route, permute, expert FFN, combine, enqueued on `stream`.
+ * Sources: Jamba-1.5 paper, "Model Architecture" (an MoE module with n
+ * experts, top K per token, in place of the MLP) and "Serving Considerations
+ * and Improvements" (ExpertsInt8: int8 expert weights dequantized to BF16
+ * inside the fused kernel).
  * Bit-identical to the four staged calls above with the same ffn_path.
  *   topk_ids_out [T, K] / topk_w_out [T, K]: optional copies of the routing (NULL to skip)
  *   workspace    >= moe_workspace_size bytes */

@@ -114,17 +114,26 @@ def silu(z) -> np.ndarray:
     return z / (1.0 + np.exp(-z))
 
 
-def expert_swiglu(xrows, q_gate, s_gate, q_up, s_up, q_down, s_down) -> np.ndarray:
-    """One expert on a block of rows: xrows [n, d] -> [n, d], fp64.
+def expert_hidden(xrows, q_gate, s_gate, q_up, s_up) -> np.ndarray:
+    """The gated hidden activation of one expert: xrows [n, d] -> h [n, c], fp64.
 
-    g = s_g * (x @ q_g^T), u = s_u * (x @ q_u^T), h = silu(g) * u,
-    o = s_d * (h @ q_d^T). Scales are per output channel, so they multiply the
-    columns of each product.
+    g = s_g * (x @ q_g^T), u = s_u * (x @ q_u^T), h = silu(g) * u, for the c
+    output channels (rows) of q_gate / q_up given; each channel of h depends
+    only on its own row of each matrix, so any subset of channels may be passed.
     """
     x = _f64(xrows)
     g = (x @ _f64(q_gate).T) * _f64(s_gate)[None, :]
     u = (x @ _f64(q_up).T) * _f64(s_up)[None, :]
-    h = silu(g) * u
+    return silu(g) * u
+
+
+def expert_swiglu(xrows, q_gate, s_gate, q_up, s_up, q_down, s_down) -> np.ndarray:
+    """One expert on a block of rows: xrows [n, d] -> [n, d], fp64.
+
+    h = expert_hidden(x) over all f channels, o = s_d * (h @ q_d^T). Scales are
+    per output channel, so they multiply the columns of each product.
+    """
+    h = expert_hidden(xrows, q_gate, s_gate, q_up, s_up)
     return (h @ _f64(q_down).T) * _f64(s_down)[None, :]
 
 

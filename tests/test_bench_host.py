@@ -83,3 +83,31 @@ def test_more_than_one_gpu_is_refused():
                        text=True, cwd=ROOT, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_spread_quantiles():
+    s = bench.spread([float(i) for i in range(1, 12)])     # 1..11
+    assert s["p50_ms"] == 6.0 and s["p10_ms"] == 2.0 and s["p90_ms"] == 10.0
+
+
+def test_default_workload_is_the_largest_single_gpu_config(monkeypatch):
+    monkeypatch.setattr(sys, "argv", ["bench.py"])
+    a = bench.parse()
+    assert a.workload == "large-prefill-skewed" and a.gpus == 1
+    assert bench.SIBLING["large-prefill-skewed"] == "large-decode"
+    assert bench.SIBLING["large-decode"] == "large-prefill-skewed"
+
+
+def test_cpu_baseline_fit_on_a_small_workload():
+    """The oracle baseline runs on the host: every field present, cores from the affinity mask."""
+    import types
+    w = workloads.TINY.with_(T=96)
+    x = workloads.draw_activations(w)
+    wr, bias = workloads.draw_router(w)
+    src = workloads.draw_expert_weights(w, "cpu")
+    layer = types.SimpleNamespace(router_w=wr, bias=bias)
+    r = bench.cpu_baseline(w, x, layer, src, experts_sampled=(0, 3), rows_fit=(2, 8))
+    assert r["kind"] == "oracle" and r["unit"] == "tokens/s" and r["dtype"] == "f64"
+    assert r["cores"] == len(os.sched_getaffinity(0))
+    assert r["value"] > 0 and r["step_ms_estimate"] > 0 and r["gflops"] > 0
+    assert "a + b*rows" in r["sample"]

@@ -184,6 +184,75 @@ def test_expert_ffn_matches_oracle(path, T, d, f, E, K, act, scale, routing):
     assert_close_to_oracle(np64(y_rows), ref_rows, "y_rows")
 
 
+@pytest.mark.parametrize("path", [MOE_PATH_AUTO, MOE_PATH_TILED])
+def test_long_and_short_experts_in_one_launch(path):
+    """One expert with more than 24 row tiles of 128 rows (its gate/up row tiles are
+    visited in groups of up to 16) in the same launch as experts with fewer (groups
+    of up to 8), every segment with a ragged last tile, and ragged channel tiles
+    (f = 320: 2.5 gate/up channel tiles; d = 192: three quarters of a down tile).
+    Every row of y_rows and every token of y against the oracle."""
+    T, d, f, E, K = 4000, 192, 320, 4, 2
+    w, x, wr, b, W = _case(T, d, f, E, K, "bf16", "bf16", bias=[8.0, 0.0, 0.0, 0.0], seed=21)
+    ex = experts_to_device(W, torch.bfloat16)
+    xg, wrg, bg = x.cuda(), wr.cuda(), b.cuda()
+    y, ids, gw = moe_forward(xg, wrg, bg, ex, K, path=path)
+    off, ss, s2r = moe_permute(ids, E)
+    rows = moe_expert_ffn(xg, off, ss, ex, K, path=path)
+    torch.cuda.synchronize()
+    ids_g = ids.cpu().numpy()
+    counts = np.bincount(ids_g.reshape(-1), minlength=E)
+    assert counts[0] >= 24 * 128 and np.all(counts[1:] < 24 * 128) and np.all(counts[1:] >= 128), counts
+    assert np.all(counts % 128 != 0), counts
+    x64, wr64, b64 = np64(x), np64(wr), np64(b)
+    check_routing(ids_g, gw.cpu().numpy(), omoe.router_logits(x64, wr64, b64), K)
+    o = omoe.expert_outputs(x64, ids_g, W)
+    assert_close_to_oracle(np64(rows), o.reshape(T * K, -1)[ss.cpu().numpy()], "y_rows (every row)")
+    ref = omoe.moe_forward(x64, wr64, b64, W, K, ids=ids_g)["y"]
+    assert_close_to_oracle(np64(y), ref, "y (every token)")
+
+
+def test_tiled_register_staged_bf16_past_32bit_offsets():
+    """bf16 activations whose h needs byte offsets of 2^32 and more run on the
+    register-staged tiled kernel (the direct-to-LDS kernel addresses with 32-bit
+    offsets): h = 16384 rows x 131072 channels x 2 bytes = 4 GiB exactly.
+    Sampled rows spread over every expert's segment, among them the last rows of
+    h, and sampled whole tokens, against the oracle."""
+    T, d, f, E, K = 8192, 64, 131072, 16, 2
+    w, x, wr, b, W = _case(T, d, f, E, K, "bf16", "bf16", seed=23)
+    ex = experts_to_device(W, torch.bfloat16)
+    xg, wrg = x.cuda(), wr.cuda()
+    y, ids, gw = moe_forward(xg, wrg, None, ex, K)
+    off, ss, s2r = moe_permute(ids, E)
+    rows = moe_expert_ffn(xg, off, ss, ex, K)
+    torch.cuda.synchronize()
+    ids_g = ids.cpu().numpy()
+    x64, wr64 = np64(x), np64(wr)
+    logits = omoe.router_logits(x64, wr64)
+    flags = check_routing(ids_g, gw.cpu().numpy(), logits, K)
+    off_h, ss_h = off.cpu().numpy(), ss.cpu().numpy()
+    assert int(off_h[-1]) * f * 2 >= 2 ** 32
+    rng = np.random.default_rng(3)
+    pick = []
+    for e in range(E):
+        n = off_h[e + 1] - off_h[e]
+        if n:
+            pick += [off_h[e], off_h[e + 1] - 1] + list(off_h[e] + rng.integers(0, n, size=6))
+    pick += list(range(off_h[-1] - 8, off_h[-1]))           # the highest rows of h
+    pick = np.unique(np.array(pick))
+    slots = ss_h[pick]
+    keep = np.zeros((T, K), dtype=bool)
+    keep.reshape(-1)[slots] = True
+    keep &= ~flags[:, None]
+    tok = np.nonzero(~flags)[0][-16:]                        # the last tokens, whole
+    keep[tok] = True
+    o = omoe.expert_outputs(x64, np.where(keep, ids_g, -1), W, experts=range(E))
+    tt, kk = np.nonzero(keep)
+    r_idx = s2r.cpu().numpy().reshape(T, K)[tt, kk]
+    assert_close_to_oracle(np64(rows[torch.from_numpy(r_idx.astype(np.int64)).cuda()]), o[tt, kk], "y_rows (sampled)")
+    ref_y = omoe.combine(o[tok], omoe.topk_gate(logits, K)[1][tok])
+    assert_close_to_oracle(np64(y[torch.from_numpy(tok).cuda()]), ref_y, "y (last tokens)")
+
+
 # --------------------------------------------------------------------------- combine
 @pytest.mark.parametrize("T,d,K,act", [(1, 64, 2, "bf16"), (129, 320, 2, "f32"), (40, 128, 5, "bf16")])
 def test_combine_matches_oracle(T, d, K, act):

@@ -117,6 +117,22 @@ def test_single_expert_is_textbook_swiglu_mlp():
     np.testing.assert_allclose(out["y"], ref.numpy(), rtol=1e-12, atol=1e-12)
 
 
+def test_expert_hidden_is_textbook_gated_activation_on_any_channel_subset():
+    """h = silu(x W_g^T) * (x W_u^T) on the dequantized weights (torch CPU fp64), and a
+    subset of channels gives the same columns as the whole matrix."""
+    rng = np.random.default_rng(15)
+    x, _, _, W = _make_layer(rng, T=7, d=32, f=40, E=1)
+    h = moe.expert_hidden(x, W["q_gate"][0], W["s_gate"][0], W["q_up"][0], W["s_up"][0])
+    deq = {k: torch.from_numpy(W["q_" + k].astype(np.float64)[0]) * torch.from_numpy(W["s_" + k][0])[:, None]
+           for k in ("gate", "up")}
+    xt = torch.from_numpy(x)
+    ref = torch.nn.functional.silu(xt @ deq["gate"].T) * (xt @ deq["up"].T)
+    np.testing.assert_allclose(h, ref.numpy(), rtol=1e-12, atol=1e-12)
+    ch = np.array([39, 0, 17, 17, 5])
+    hs = moe.expert_hidden(x, W["q_gate"][0][ch], W["s_gate"][0][ch], W["q_up"][0][ch], W["s_up"][0][ch])
+    np.testing.assert_allclose(hs, h[:, ch], rtol=1e-12, atol=1e-14)   # BLAS may sum in another order
+
+
 def test_k_equals_e_is_dense_mixture():
     rng = np.random.default_rng(15)
     x, wr, _, W = _make_layer(rng, T=6, d=16, f=24, E=5)

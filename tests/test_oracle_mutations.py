@@ -36,6 +36,13 @@ def _swiglu_swapped(xrows, q_gate, s_gate, q_up, s_up, q_down, s_down):
     return ((g * moe.silu(u)) @ q_down.T.astype(np.float64)) * s_down[None, :]
 
 
+def _hidden_up_scale_from_gate(xrows, q_gate, s_gate, q_up, s_up):
+    x = np.asarray(xrows, dtype=np.float64)
+    g = (x @ q_gate.T.astype(np.float64)) * s_gate[None, :]
+    u = (x @ q_up.T.astype(np.float64)) * s_gate[None, :]
+    return moe.silu(g) * u
+
+
 def _silu_wrong_sign(z):
     z = np.asarray(z, dtype=np.float64)
     return z / (1.0 + np.exp(z))
@@ -150,6 +157,8 @@ MUTATIONS = [
     ("moe", "expert_swiglu", _swiglu_no_up_scale, [pm.test_single_expert_is_textbook_swiglu_mlp]),
     ("moe", "expert_swiglu", _swiglu_swapped, [pm.test_single_expert_is_textbook_swiglu_mlp]),
     ("moe", "silu", _silu_wrong_sign, [pm.test_single_expert_is_textbook_swiglu_mlp]),
+    ("moe", "expert_hidden", _hidden_up_scale_from_gate,
+     [pm.test_expert_hidden_is_textbook_gated_activation_on_any_channel_subset]),
     ("moe", "topk_gate", _gate_no_renorm, [pm.test_top2_weights_are_logistic_of_gap]),
     ("moe", "topk_gate", _gate_ties_high, [pm.test_exact_ties_go_to_lower_index]),
     ("moe", "combine", _combine_swapped, [pm.test_vectorised_layer_matches_scalar_loop]),
