@@ -216,6 +216,23 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const void* router
                        void* y, int32_t* topk_ids_out, float* topk_w_out,
                        void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* moe_forward without a caller workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc). Same arguments and results as moe_forward (bit for
+ * bit), minus the workspace: the library keeps a fixed 32 MiB scratch array in
+ * device memory on each GPU it runs on (held until the process ends) and uses
+ * it as the workspace. A shape whose moe_workspace_size exceeds 32 MiB is
+ * rejected with MOE_ERR_WORKSPACE before anything is enqueued (every
+ * decode-sized layer fits: Jamba-1.5-Large at T=64 needs about 11 MiB). The
+ * call allocates nothing. All calls on one GPU share that GPU's scratch, which
+ * keeps the last call's contents: calls that overlap on one GPU (concurrent
+ * streams, or host threads) race and must be serialised by the caller. */
+moe_status moe_forward_noalloc(const moe_shape* shape, const void* x, const void* router_w,
+                               const float* router_bias,
+                               const void* w_gate, const void* w_up, const void* w_down,
+                               const void* s_gate, const void* s_up, const void* s_down,
+                               void* y, int32_t* topk_ids_out, float* topk_w_out, hipStream_t stream);
+
 /* Dense int8-weight MLP (Jamba-1.5 paper, "Serving Considerations and
  * Improvements": ExpertsInt8 quantizes the MoE *and* the MLP weights). An MLP
  * layer is the MoE layer with one expert used by every token with weight 1:

@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "../../include/moe_int8.h"
 #include "kernels.h"
@@ -168,6 +169,101 @@ moe_status check_quantize(int64_t rows, int32_t cols, int32_t src_dtype, const v
   REQUIRE_PTR(q);
   if (!s) return fail(MOE_ERR_NULL, "s is NULL");
   if ((reinterpret_cast<uintptr_t>(s) & 3u) != 0) return fail(MOE_ERR_ALIGN, "s is not 4-byte aligned");
+  return MOE_OK;
+}
+
+// ---------------------------------------------------------------- fixed scratch of moe_forward_noalloc
+// The allocation-free entry point keeps its workspace in this file-scope
+// device array. Each GPU the library runs on holds its own copy until the
+// process ends. In host code the name stands for a host-side shadow, not a
+// device address: the device address is looked up once per device with
+// hipGetSymbolAddress (with that device current) and kept in g_scratch_ptr.
+constexpr size_t kScratchBytes = size_t(32) << 20;   // 32 MiB: the decode-sized layers
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+moe_status scratch_on_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(MOE_ERR_UNSUPPORTED, "device %d beyond the library's %d", dev, kMaxDevices);
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+      if (!p) return fail(MOE_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return MOE_OK;
+}
+
+moe_status forward_impl(const moe_shape* s, const void* x, const void* router_w, const float* router_bias,
+                       const void* w_gate, const void* w_up, const void* w_down, const void* s_gate,
+                       const void* s_up, const void* s_down, void* y, int32_t* topk_ids_out, float* topk_w_out,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  st = check_ffn(s);
+  if (st != MOE_OK) return st;
+  if (s->T == 0) return MOE_OK;   // nothing is read or written
+  REQUIRE_PTR(x);
+  REQUIRE_PTR(router_w);
+  REQUIRE_PTR(w_gate);
+  REQUIRE_PTR(w_up);
+  REQUIRE_PTR(w_down);
+  REQUIRE_SCALE(s, s_gate);
+  REQUIRE_SCALE(s, s_up);
+  REQUIRE_SCALE(s, s_down);
+  REQUIRE_PTR(y);
+  REQUIRE_PTR(workspace);
+  if (router_bias && !aligned16(router_bias)) return fail(MOE_ERR_ALIGN, "router_bias is not 16-byte aligned");
+  if (topk_ids_out && !aligned16(topk_ids_out)) return fail(MOE_ERR_ALIGN, "topk_ids_out is not 16-byte aligned");
+  if (topk_w_out && !aligned16(topk_w_out)) return fail(MOE_ERR_ALIGN, "topk_w_out is not 16-byte aligned");
+  const WsLayout L = forward_layout(s);
+  if (workspace_bytes < L.total)
+    return fail(MOE_ERR_WORKSPACE, "workspace_bytes=%zu < required %zu", workspace_bytes, L.total);
+
+  char* ws = static_cast<char*>(workspace);
+  int32_t* ids = topk_ids_out ? topk_ids_out : reinterpret_cast<int32_t*>(ws + L.ids);
+  float* wts = topk_w_out ? topk_w_out : reinterpret_cast<float*>(ws + L.w);
+  int32_t* offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
+  int32_t* sorted = reinterpret_cast<int32_t*>(ws + L.sorted);
+  int32_t* s2r = reinterpret_cast<int32_t*>(ws + L.s2r);
+  __bf16* h = reinterpret_cast<__bf16*>(ws + L.h);
+  float* y_rows = reinterpret_cast<float*>(ws + L.y_rows);
+
+  hipError_t e = moe::launch_router(x, router_w, router_bias, s->T, s->d, s->E, s->K, s->act_dtype == MOE_BF16,
+                                    ids, wts, stream);
+  if (e != hipSuccess) return hip_fail(e, "router launch");
+  moe::FfnArgs a = ffn_args(s, x, offsets, sorted, w_gate, w_up, w_down, s_gate, s_up, s_down, y_rows, h);
+  if (L.part_bytes) a.part = reinterpret_cast<float*>(ws + L.part);
+  if (use_stream(s) && moe::stream_gate_up_takes_ids((long)s->T * s->K, s->E)) {
+    // at most 256 slots: the gate/up pass derives the permutation from the ids
+    // and writes it for the down pass and the combine (one launch fewer)
+    a.ids = ids;
+    a.perm_offsets = offsets;
+    a.perm_sorted = sorted;
+    a.perm_s2r = s2r;
+    st = run_gate_up(s, a, stream);
+    a.ids = nullptr;
+  } else {
+    e = moe::launch_permute(ids, s->T * s->K, s->E, offsets, sorted, s2r, stream);
+    if (e != hipSuccess) return hip_fail(e, "permute launch");
+    st = run_gate_up(s, a, stream);
+  }
+  if (st != MOE_OK) return st;
+  st = run_down(s, a, stream);
+  if (st != MOE_OK) return st;
+  e = moe::launch_combine(y_rows, s2r, wts, s->T, s->d, s->K, s->act_dtype == MOE_BF16, y, stream);
+  if (e != hipSuccess) return hip_fail(e, "combine launch");
   return MOE_OK;
 }
 
@@ -344,62 +440,26 @@ moe_status moe_forward(const moe_shape* s, const void* x, const void* router_w, 
                        const void* w_gate, const void* w_up, const void* w_down, const void* s_gate,
                        const void* s_up, const void* s_down, void* y, int32_t* topk_ids_out, float* topk_w_out,
                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return forward_impl(s, x, router_w, router_bias, w_gate, w_up, w_down, s_gate, s_up, s_down, y, topk_ids_out,
+                      topk_w_out, workspace, workspace_bytes, stream);
+}
+
+moe_status moe_forward_noalloc(const moe_shape* s, const void* x, const void* router_w, const float* router_bias,
+                               const void* w_gate, const void* w_up, const void* w_down, const void* s_gate,
+                               const void* s_up, const void* s_down, void* y, int32_t* topk_ids_out,
+                               float* topk_w_out, hipStream_t stream) {
   moe_status st = check_shape(s);
   if (st != MOE_OK) return st;
-  st = check_ffn(s);
+  const size_t need = forward_layout(s).total;
+  if (need > kScratchBytes)
+    return fail(MOE_ERR_WORKSPACE, "moe_forward_noalloc: this shape needs %zu bytes of scratch, more than the "
+                "library's fixed %zu (use moe_forward with a caller workspace)", need, kScratchBytes);
+  if (s->T == 0) return MOE_OK;
+  void* ws = nullptr;
+  st = scratch_on_current_device(&ws);
   if (st != MOE_OK) return st;
-  if (s->T == 0) return MOE_OK;   // nothing is read or written
-  REQUIRE_PTR(x);
-  REQUIRE_PTR(router_w);
-  REQUIRE_PTR(w_gate);
-  REQUIRE_PTR(w_up);
-  REQUIRE_PTR(w_down);
-  REQUIRE_SCALE(s, s_gate);
-  REQUIRE_SCALE(s, s_up);
-  REQUIRE_SCALE(s, s_down);
-  REQUIRE_PTR(y);
-  REQUIRE_PTR(workspace);
-  if (router_bias && !aligned16(router_bias)) return fail(MOE_ERR_ALIGN, "router_bias is not 16-byte aligned");
-  if (topk_ids_out && !aligned16(topk_ids_out)) return fail(MOE_ERR_ALIGN, "topk_ids_out is not 16-byte aligned");
-  if (topk_w_out && !aligned16(topk_w_out)) return fail(MOE_ERR_ALIGN, "topk_w_out is not 16-byte aligned");
-  const WsLayout L = forward_layout(s);
-  if (workspace_bytes < L.total)
-    return fail(MOE_ERR_WORKSPACE, "workspace_bytes=%zu < required %zu", workspace_bytes, L.total);
-
-  char* ws = static_cast<char*>(workspace);
-  int32_t* ids = topk_ids_out ? topk_ids_out : reinterpret_cast<int32_t*>(ws + L.ids);
-  float* wts = topk_w_out ? topk_w_out : reinterpret_cast<float*>(ws + L.w);
-  int32_t* offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
-  int32_t* sorted = reinterpret_cast<int32_t*>(ws + L.sorted);
-  int32_t* s2r = reinterpret_cast<int32_t*>(ws + L.s2r);
-  __bf16* h = reinterpret_cast<__bf16*>(ws + L.h);
-  float* y_rows = reinterpret_cast<float*>(ws + L.y_rows);
-
-  hipError_t e = moe::launch_router(x, router_w, router_bias, s->T, s->d, s->E, s->K, s->act_dtype == MOE_BF16,
-                                    ids, wts, stream);
-  if (e != hipSuccess) return hip_fail(e, "router launch");
-  moe::FfnArgs a = ffn_args(s, x, offsets, sorted, w_gate, w_up, w_down, s_gate, s_up, s_down, y_rows, h);
-  if (L.part_bytes) a.part = reinterpret_cast<float*>(ws + L.part);
-  if (use_stream(s) && moe::stream_gate_up_takes_ids((long)s->T * s->K, s->E)) {
-    // at most 256 slots: the gate/up pass derives the permutation from the ids
-    // and writes it for the down pass and the combine (one launch fewer)
-    a.ids = ids;
-    a.perm_offsets = offsets;
-    a.perm_sorted = sorted;
-    a.perm_s2r = s2r;
-    st = run_gate_up(s, a, stream);
-    a.ids = nullptr;
-  } else {
-    e = moe::launch_permute(ids, s->T * s->K, s->E, offsets, sorted, s2r, stream);
-    if (e != hipSuccess) return hip_fail(e, "permute launch");
-    st = run_gate_up(s, a, stream);
-  }
-  if (st != MOE_OK) return st;
-  st = run_down(s, a, stream);
-  if (st != MOE_OK) return st;
-  e = moe::launch_combine(y_rows, s2r, wts, s->T, s->d, s->K, s->act_dtype == MOE_BF16, y, stream);
-  if (e != hipSuccess) return hip_fail(e, "combine launch");
-  return MOE_OK;
+  return forward_impl(s, x, router_w, router_bias, w_gate, w_up, w_down, s_gate, s_up, s_down, y, topk_ids_out,
+                      topk_w_out, ws, kScratchBytes, stream);
 }
 
 moe_status moe_mlp_workspace_size(const moe_shape* shape, size_t* bytes) {

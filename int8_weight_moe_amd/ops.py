@@ -249,6 +249,29 @@ def moe_forward(x: torch.Tensor, router_w: torch.Tensor, bias: Optional[torch.Te
     return y, ids, w
 
 
+def moe_forward_noalloc(x: torch.Tensor, router_w: torch.Tensor, bias: Optional[torch.Tensor],
+                        experts: Int8Experts, K: int, path: int = MOE_PATH_AUTO, y: torch.Tensor = None,
+                        ids: torch.Tensor = None, w: torch.Tensor = None):
+    """The whole layer on the library's fixed per-GPU scratch (no workspace argument;
+    the C call allocates nothing). Outputs y, ids and w must be given by the caller
+    that cannot allocate; they are allocated here only when omitted."""
+    lib = _lib_handle()
+    T, d = x.shape
+    shape = make_shape(T, d, experts.f, experts.E, K, x.dtype, experts.scale_dtype, path, experts.fmt)
+    dev = x.device
+    if y is None:
+        y = torch.empty((T, d), dtype=x.dtype, device=dev)
+    if ids is None:
+        ids = torch.empty((T, K), dtype=torch.int32, device=dev)
+    if w is None:
+        w = torch.empty((T, K), dtype=torch.float32, device=dev)
+    _lib.check(lib.moe_forward_noalloc(
+        ctypes.byref(shape), _ptr(x), _ptr(router_w), _ptr(bias), _ptr(experts.q_gate), _ptr(experts.q_up),
+        _ptr(experts.q_down), _ptr(experts.s_gate), _ptr(experts.s_up), _ptr(experts.s_down), _ptr(y), _ptr(ids),
+        _ptr(w), _stream()))
+    return y, ids, w
+
+
 def moe_mlp_forward(x: torch.Tensor, experts: Int8Experts, path: int = MOE_PATH_AUTO,
                     y: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Dense int8-weight SwiGLU MLP (one expert, E = K = 1). Returns y [T, d] in x.dtype."""

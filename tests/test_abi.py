@@ -217,3 +217,16 @@ def test_weight_format_rules(lib):
                                ctypes.c_size_t(1 << 30), None) == 6
         assert b"bf16 activations" in lib.moe_last_error()
         assert lib.moe_expert_down(ctypes.byref(s), A, A, A, A, A, None, 0, None) == 6
+
+
+def test_noalloc_forward_rejects_shapes_beyond_its_scratch(lib):
+    """moe_forward_noalloc checks its fixed 32 MiB scratch before anything else is
+    touched: an oversized shape is MOE_ERR_WORKSPACE with no pointer read and no
+    HIP call; T = 0 is accepted."""
+    big = _shape(T=40000, d=128, f=192, E=4, K=2)          # y_rows alone: 80000 x 128 x 4 bytes > 32 MiB
+    st = lib.moe_forward_noalloc(ctypes.byref(big), None, None, None, None, None, None, None, None, None,
+                                 None, None, None, None)
+    assert st == 5 and b"scratch" in lib.moe_last_error()
+    empty = _shape(T=0)
+    assert lib.moe_forward_noalloc(ctypes.byref(empty), None, None, None, None, None, None, None, None, None,
+                                   None, None, None, None) == 0
