@@ -103,7 +103,7 @@ typedef struct moe_shape {
 } moe_shape;
 
 /* ABI version of this header (bumped on any signature change). */
-#define MOE_ABI_VERSION 4
+#define MOE_ABI_VERSION 5
 int32_t moe_abi_version(void);
 
 /* Static description of a status code. */
@@ -113,19 +113,20 @@ const char* moe_status_str(moe_status status);
 const char* moe_last_error(void);
 
 /* Workspace, in bytes, that moe_forward needs for this shape (includes the
- * routing buffers, the permutation, h, y_rows and the down pass's partial
- * sums, see moe_down_workspace_size). */
+ * routing buffers, the permutation, h, y_rows and the down pass's own
+ * workspace, see moe_down_workspace_size). */
 moe_status moe_workspace_size(const moe_shape* shape, size_t* bytes);
 
 /* Workspace, in bytes, that moe_expert_ffn needs: h (T*K*f bf16), then the
- * down pass's partial sums (moe_down_workspace_size), each padded to 256. */
+ * down pass's workspace (moe_down_workspace_size), each padded to 256. */
 moe_status moe_ffn_workspace_size(const moe_shape* shape, size_t* bytes);
 
-/* Workspace, in bytes, that the down pass can use: fp32 partial sums
- * [planes, T*K, d] for shapes whose weight-streaming down pass splits its
- * reduction over workgroups (33 to 64 rows per expert on average and too few
- * output-channel groups to fill the GPU, e.g. a dense MLP at decode); 0 for
- * every other shape. */
+/* Workspace, in bytes, that the down pass can use:
+ *   - STREAM schedule: fp32 partial sums [planes, T*K, d] for shapes whose
+ *     weight-streaming down pass splits its reduction over workgroups (33 to
+ *     64 rows per expert on average and too few output-channel groups to fill
+ *     the GPU, e.g. a dense MLP at decode); 0 for every other stream shape;
+ *   - TILED schedule: 256 bytes of tile claim words (see moe_expert_down). */
 moe_status moe_down_workspace_size(const moe_shape* shape, size_t* bytes);
 
 /* Router and gate (paper: "Model Architecture", top K of n experts per token).
@@ -175,14 +176,20 @@ moe_status moe_expert_ffn(const moe_shape* shape, const void* x,
  * source as moe_expert_ffn: Jamba-1.5 paper, "Serving Considerations and
  * Improvements"):
  * gate/up  h[r] = silu(s_g * (q_g . x_r)) * (s_u * (q_u . x_r))  for every sorted row r,
- *          h [T*K, f] bf16 out (rows past off[E] untouched);
+ *          h [T*K, f] bf16 out (rows past off[E] untouched).
  * down     y_rows[r] = s_d * (q_d . h[r]),  h [T*K, f] bf16 in, y_rows [T*K, d] fp32 out.
- *          workspace: NULL, or 16-byte aligned and >= moe_down_workspace_size
- *          bytes (else MOE_ERR_ALIGN / MOE_ERR_WORKSPACE). With it, a down pass
- *          that splits its reduction may spread the slices over workgroups
- *          (partial sums in the workspace, added in slice order by a second
- *          kernel); without it the slices stay inside one workgroup. y_rows is
- *          the same bit for bit either way.
+ *          workspace: NULL, or 16-byte aligned and at least
+ *          moe_down_workspace_size bytes (else MOE_ERR_ALIGN /
+ *          MOE_ERR_WORKSPACE). Its contents need not be initialised. With it:
+ *          - on the TILED schedule, the pass's workgroups claim their tiles
+ *            through atomic counters in the workspace (cleared by the pass
+ *            itself) and XCDs that run faster take more tiles; without it
+ *            every workgroup's tile is fixed by its id;
+ *          - on the STREAM schedule, a down pass that splits its reduction
+ *            may spread the slices over workgroups (partial sums in the
+ *            workspace, added in slice order by a second kernel); without it
+ *            the slices stay inside one workgroup.
+ *          The results are the same bit for bit either way.
  * moe_expert_ffn is moe_expert_gate_up followed by moe_expert_down on the same
  * stream, with the part of its workspace after h as the down workspace. */
 moe_status moe_expert_gate_up(const moe_shape* shape, const void* x, const int32_t* expert_offsets,

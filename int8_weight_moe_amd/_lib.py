@@ -11,7 +11,7 @@ import os
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libmoe_int8.so")
 
-ABI_VERSION = 4
+ABI_VERSION = 5
 MOE_OK = 0
 STATUS_NAMES = {
     0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_DTYPE", 4: "MOE_ERR_ALIGN",

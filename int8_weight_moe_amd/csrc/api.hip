@@ -63,7 +63,7 @@ moe_status check_shape(const moe_shape* s) {
   } while (0)
 
 struct WsLayout {
-  size_t ids, w, offsets, sorted, s2r, h, y_rows, part, part_bytes, total;
+  size_t ids, w, offsets, sorted, s2r, h, y_rows, part, part_bytes, claims, total;
 };
 
 bool use_stream(const moe_shape* s);
@@ -81,20 +81,25 @@ WsLayout forward_layout(const moe_shape* s) {
   L.h = o;       o += round_up(S * (size_t)s->f * 2);
   L.y_rows = o;  o += round_up(S * (size_t)s->d * 4);
   // partial sums of a stream down pass split over workgroups (none otherwise)
-  L.part_bytes = down_ws_bytes(s);
+  L.part_bytes = use_stream(s) ? down_ws_bytes(s) : 0;
   L.part = o;    o += round_up(L.part_bytes);
+  // tile claim words of the tiled down pass (none for the stream schedule)
+  L.claims = o;  o += use_stream(s) ? 0 : moe::kTileClaimBytes;
   L.total = o;
   return L;
 }
 
-// fp32 partial sums of a stream down pass split over workgroups ([planes, S, d]), 0 if it does not split.
+// Workspace of the down pass: the stream schedule's fp32 partial sums of a
+// reduction split over workgroups ([planes, S, d]; 0 bytes if it does not
+// split), or the tiled schedule's tile claim words.
 size_t down_ws_bytes(const moe_shape* s) {
+  if (!use_stream(s)) return moe::kTileClaimBytes;
   const long S = (long)s->T * s->K;
-  const int planes = use_stream(s) ? moe::stream_down_planes(S, s->d, s->f, s->E) : 0;
+  const int planes = moe::stream_down_planes(S, s->d, s->f, s->E);
   return (size_t)planes * (size_t)S * (size_t)s->d * 4;
 }
 
-// moe_expert_ffn: h, then the down pass's partial sums
+// moe_expert_ffn: h, then the down pass's workspace
 size_t ffn_h_bytes(const moe_shape* s) { return round_up((size_t)s->T * s->K * (size_t)s->f * 2); }
 size_t ffn_ws_bytes(const moe_shape* s) { return ffn_h_bytes(s) + round_up(down_ws_bytes(s)); }
 
@@ -138,6 +143,7 @@ moe::FfnArgs ffn_args(const moe_shape* s, const void* x, const int32_t* offsets,
   a.part = nullptr;
   a.ids = nullptr;
   a.perm_offsets = a.perm_sorted = a.perm_s2r = nullptr;
+  a.claims_down = nullptr;
   a.T = s->T;
   a.d = s->d;
   a.f = s->f;
@@ -245,6 +251,7 @@ moe_status forward_impl(const moe_shape* s, const void* x, const void* router_w,
   if (e != hipSuccess) return hip_fail(e, "router launch");
   moe::FfnArgs a = ffn_args(s, x, offsets, sorted, w_gate, w_up, w_down, s_gate, s_up, s_down, y_rows, h);
   if (L.part_bytes) a.part = reinterpret_cast<float*>(ws + L.part);
+  if (!use_stream(s)) a.claims_down = reinterpret_cast<unsigned long long*>(ws + L.claims);
   if (use_stream(s) && moe::stream_gate_up_takes_ids((long)s->T * s->K, s->E)) {
     // at most 256 slots: the gate/up pass derives the permutation from the ids
     // and writes it for the down pass and the combine (one launch fewer)
@@ -361,7 +368,12 @@ moe_status moe_expert_ffn(const moe_shape* s, const void* x, const int32_t* expe
     return fail(MOE_ERR_WORKSPACE, "workspace_bytes=%zu < required %zu", workspace_bytes, need);
   moe::FfnArgs a = ffn_args(s, x, expert_offsets, sorted_slots, w_gate, w_up, w_down, s_gate, s_up, s_down, y_rows,
                             static_cast<__bf16*>(workspace));
-  if (down_ws_bytes(s)) a.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + ffn_h_bytes(s));
+  char* dws = static_cast<char*>(workspace) + ffn_h_bytes(s);
+  if (use_stream(s)) {
+    if (down_ws_bytes(s)) a.part = reinterpret_cast<float*>(dws);
+  } else {
+    a.claims_down = reinterpret_cast<unsigned long long*>(dws);
+  }
   st = run_gate_up(s, a, stream);
   if (st != MOE_OK) return st;
   return run_down(s, a, stream);
@@ -409,7 +421,13 @@ moe_status moe_expert_down(const moe_shape* s, const void* h, const int32_t* exp
   }
   moe::FfnArgs a = ffn_args(s, nullptr, expert_offsets, nullptr, nullptr, nullptr, w_down, nullptr, nullptr, s_down,
                             y_rows, static_cast<__bf16*>(const_cast<void*>(h)));
-  if (workspace && need) a.part = static_cast<float*>(workspace);
+  if (workspace && need) {
+    if (use_stream(s)) {
+      a.part = static_cast<float*>(workspace);
+    } else {
+      a.claims_down = static_cast<unsigned long long*>(workspace);
+    }
+  }
   return run_down(s, a, stream);
 }
 
@@ -503,6 +521,7 @@ moe_status moe_mlp_forward(const moe_shape* s, const void* x, const void* w_gate
   if (e != hipSuccess) return hip_fail(e, "dense init launch");
   moe::FfnArgs a = ffn_args(s, x, offsets, sorted, w_gate, w_up, w_down, s_gate, s_up, s_down, y_rows, h);
   if (L.part_bytes) a.part = reinterpret_cast<float*>(ws + L.part);
+  if (!use_stream(s)) a.claims_down = reinterpret_cast<unsigned long long*>(ws + L.claims);
   st = run_gate_up(s, a, stream);
   if (st != MOE_OK) return st;
   st = run_down(s, a, stream);

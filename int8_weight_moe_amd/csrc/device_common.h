@@ -76,66 +76,74 @@ constexpr int waitcnt_vm_lgkm0(int vm) { return (vm & 15) | ((vm >> 4) << 14) | 
 // instead of walking the experts one dependent load at a time; every lane of
 // the wave returns the same (wave-uniform) answer.
 
-// Tile of this workgroup in the expert-grouped rows x output-channel tiles
+// Tiles of a grouped pass: the expert-grouped rows x output-channel tiles
 // grid, where expert x owns ceil(count_x / BM) consecutive row tiles.
-//   - The real tile count (row tiles x n_tiles) comes from the offsets, and
-//     block b works on tile (b % xcds) * per_xcd + b / xcds with per_xcd =
-//     ceil(count / xcds) rounded up to a multiple of `grain`: workgroups are
-//     dealt to the XCDs in turn, so every XCD gets a contiguous share of the
-//     real tiles, equal up to the grain (sizing the shares by the grid, which
-//     is launched for the most row tiles the slot count allows, left the last
-//     XCD idle for the tiles that do not exist). The grid must hold
-//     xcds * per_xcd blocks.
+//   - The real tile count (row tiles x n_tiles) comes from the offsets. The
+//     tiles are cut into 8 XCD queues, contiguous ranges of per_xcd tiles
+//     (the count divided by the XCDs, rounded up to a multiple of `grain`), so
+//     each XCD works on a contiguous range and keeps its operands in its own
+//     L2 (sizing the queues by the grid, which is launched for the most row
+//     tiles the slot count allows, left the last XCD idle for the tiles that
+//     do not exist).
 //   - Each expert's row tiles form groups of at most GM (GM_LONG for an
 //     expert with at least 3*GM row tiles; as even as possible; no group spans
-//     two experts), and a group takes every channel
-//     tile before the next group, so a weight tile is read by all the row
-//     tiles of its group in a row. (Groups of GM over all row tiles, which
-//     span expert boundaries and then read two experts' weights, measured
-//     1-1.5% slower on the Mini prefill passes.)
-// Returns false for blocks past the real tiles; else the expert, first row,
-// row count and channel tile.
-template <int BM, int GM, int GM_LONG = GM>
-__device__ __forceinline__ bool block_tile(const int32_t* __restrict__ offsets, int E, int n_tiles_n, int xcds,
-                                           int grain, int& e, int& row0, int& nrows, int& nt) {
+//     two experts), and a group takes every channel tile before the next
+//     group, so a weight tile is read by all the row tiles of its group in a
+//     row. (Groups of GM over all row tiles, which span expert boundaries and
+//     then read two experts' weights, measured 1-1.5% slower on the Mini
+//     prefill passes.)
+// Per-workgroup view of that grid, one expert per lane.
+struct TileGrid {
+  int o0, o1, tiles, excl;   // lane x: expert x's rows [o0, o1), its row tiles, the row tiles before it
+  int total, per_xcd;        // wave-uniform
+};
+
+template <int BM>
+__device__ __forceinline__ TileGrid tile_grid(const int32_t* __restrict__ offsets, int E, int n_tiles_n, int xcds,
+                                              int grain) {
   const int lane = threadIdx.x & (kWave - 1);
-  int o0 = 0, o1 = 0;
+  TileGrid g;
+  g.o0 = 0;
+  g.o1 = 0;
   if (lane < E) {
-    o0 = offsets[lane];
-    o1 = offsets[lane + 1];
+    g.o0 = offsets[lane];
+    g.o1 = offsets[lane + 1];
   }
-  const int tiles = (o1 - o0 + BM - 1) / BM;
-  int incl = tiles;   // inclusive scan of the tile counts over the lanes
+  g.tiles = (g.o1 - g.o0 + BM - 1) / BM;
+  int incl = g.tiles;   // inclusive scan of the tile counts over the lanes
 #pragma unroll
   for (int d = 1; d < kWave; d <<= 1) {
     const int v = __shfl_up(incl, d);
     if (lane >= d) incl += v;
   }
-  const int excl = incl - tiles;
-  const int m_tiles = __builtin_amdgcn_readlane(incl, kWave - 1);
-  const int total = m_tiles * n_tiles_n;
-  const int per_xcd = ((total + xcds - 1) / xcds + grain - 1) / grain * grain;
-  const int k = blockIdx.x / xcds;
-  if (k >= per_xcd) return false;
-  const int tile = (blockIdx.x % xcds) * per_xcd + k;
-  if (tile >= total) return false;
-  // the expert owning the tile (expert x owns tiles [excl_x, incl_x) * n_tiles),
-  // then the tile's balanced group of at most GM of that expert's row tiles:
-  // ceil(mt / GM) groups whose sizes differ by at most one, the larger first
-  const uint64_t hit = __ballot(lane < E && tile >= excl * n_tiles_n && tile < incl * n_tiles_n);
+  g.excl = incl - g.tiles;
+  g.total = __builtin_amdgcn_readlane(incl, kWave - 1) * n_tiles_n;
+  g.per_xcd = ((g.total + xcds - 1) / xcds + grain - 1) / grain * grain;
+  return g;
+}
+
+// Expert, first row, row count and channel tile of tile `tile` (0 <= tile < total):
+// the expert owning it (expert x owns tiles [excl_x, excl_x + tiles_x) * n_tiles),
+// then its balanced group of at most GM of that expert's row tiles:
+// ceil(mt / GM) groups whose sizes differ by at most one, the larger first.
+template <int BM, int GM, int GM_LONG = GM>
+__device__ __forceinline__ void decode_tile(const TileGrid& g, int tile, int E, int n_tiles_n, int& e, int& row0,
+                                            int& nrows, int& nt) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const uint64_t hit = __ballot(lane < E && tile >= g.excl * n_tiles_n && tile < (g.excl + g.tiles) * n_tiles_n);
   const int x = __builtin_amdgcn_readfirstlane(__ffsll((unsigned long long)hit) - 1);
-  const int mt_e = __shfl(tiles, x);
-  const int local = tile - __shfl(excl, x) * n_tiles_n;
+  const int mt_e = __shfl(g.tiles, x);
+  const int local = tile - __shfl(g.excl, x) * n_tiles_n;
   const int gmax = (mt_e >= 3 * GM) ? GM_LONG : GM;   // experts with many row tiles: larger groups
   const int ngroups = (mt_e + gmax - 1) / gmax;
   const int gbase = mt_e / ngroups, gextra = mt_e - gbase * ngroups;
   const int big = (gbase + 1) * n_tiles_n;
   int start_m, gm, in_group;
   if (local < gextra * big) {
-    const int g = local / big;
+    const int gi = local / big;
     gm = gbase + 1;
-    start_m = g * gm;
-    in_group = local - g * big;
+    start_m = gi * gm;
+    in_group = local - gi * big;
   } else {
     const int l2 = local - gextra * big;
     const int g2 = l2 / (gbase * n_tiles_n);
@@ -143,10 +151,51 @@ __device__ __forceinline__ bool block_tile(const int32_t* __restrict__ offsets, 
     start_m = gextra * (gbase + 1) + g2 * gbase;
     in_group = l2 - g2 * gbase * n_tiles_n;
   }
-  nt = in_group / gm;
+  nt = __builtin_amdgcn_readfirstlane(in_group / gm);
   e = x;
-  row0 = __builtin_amdgcn_readfirstlane(__shfl(o0, x) + (start_m + in_group % gm) * BM);
-  nrows = __builtin_amdgcn_readfirstlane(min(BM, __shfl(o1, x) - row0));
+  row0 = __builtin_amdgcn_readfirstlane(__shfl(g.o0, x) + (start_m + in_group % gm) * BM);
+  nrows = __builtin_amdgcn_readfirstlane(min(BM, __shfl(g.o1, x) - row0));
+}
+
+// Static tile order: block b works on tile (b % xcds) * per_xcd + b / xcds, so
+// workgroups, which are dealt to the XCDs in turn, take their XCD's queue in
+// order. The grid must hold xcds * per_xcd blocks. -1 for blocks past the tiles.
+__device__ __forceinline__ int static_tile(const TileGrid& g, int xcds) {
+  const int k = blockIdx.x / xcds;
+  if (k >= g.per_xcd) return -1;
+  const int tile = (blockIdx.x % xcds) * g.per_xcd + k;
+  return tile < g.total ? tile : -1;
+}
+
+// Dynamic tile order (load balance across XCDs that run at different speeds):
+// a workgroup claims the next tile of its XCD's queue with one atomic
+// increment of claims[x], and once that queue is empty the next tile of the
+// other queues in turn. Every tile is claimed exactly once (each claim sees
+// the claims before it) as long as the grid has a block per tile; the grid
+// carries spare blocks so that faster XCDs can take more than their share,
+// and blocks that find every queue empty exit. claims[0..7] start at zero.
+// One lane calls it; -1 when every queue is empty.
+__device__ __forceinline__ int claim_tile(unsigned long long* __restrict__ claims, int x_home, int per_xcd,
+                                          int total) {
+  for (int i = 0; i < 8; ++i) {
+    const int x = (x_home + i) & 7;
+    const int len = min(per_xcd, total - x * per_xcd);
+    if (len <= 0) continue;
+    const int k = (int)atomicAdd(&claims[x], 1ull);
+    if (k < len) return x * per_xcd + k;
+  }
+  return -1;
+}
+
+// Tile of this workgroup in the static order (the decode of static_tile).
+// Returns false for blocks past the real tiles.
+template <int BM, int GM, int GM_LONG = GM>
+__device__ __forceinline__ bool block_tile(const int32_t* __restrict__ offsets, int E, int n_tiles_n, int xcds,
+                                           int grain, int& e, int& row0, int& nrows, int& nt) {
+  const TileGrid g = tile_grid<BM>(offsets, E, n_tiles_n, xcds, grain);
+  const int tile = static_tile(g, xcds);
+  if (tile < 0) return false;
+  decode_tile<BM, GM, GM_LONG>(g, tile, E, n_tiles_n, e, row0, nrows, nt);
   return true;
 }
 

@@ -24,9 +24,15 @@
 // Tile order: row tiles are numbered expert by expert; each expert's row
 // tiles are visited in groups of at most GM, channel tile by channel tile
 // inside a group, so the tiles that run together share a few activation tiles
-// and weight tiles of one expert. Workgroup ids are spread so that each XCD (workgroups are dealt
-// round-robin to the 8 XCDs) runs a contiguous range of that order, an equal
-// share of the real tiles, and keeps its operands in its own L2.
+// and weight tiles of one expert. That order is cut into 8 contiguous XCD
+// queues of equal length (workgroups are dealt round-robin to the 8 XCDs), so
+// each XCD keeps its operands in its own L2. With tile claim words (the down
+// pass's workspace), each workgroup of the direct-to-LDS kernel claims the next tile
+// of its XCD's queue with an atomic increment, and takes the next tile of
+// another queue once its own is empty: XCDs that run faster (the same tiles
+// took up to 5% longer on some XCDs than on others) then take more tiles.
+// Without them (and always on the gate/up pass), workgroup ids map to the
+// queues statically.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -346,7 +352,7 @@ void ffn_tiled_dma_kernel(
     const __bf16* __restrict__ X, const int32_t* __restrict__ sorted_slots, int topk,
     const int8_t* __restrict__ W0, const int8_t* __restrict__ W1, const void* __restrict__ S0,
     const void* __restrict__ S1, const int32_t* __restrict__ offsets, int E, int N, int Kd, int n_tiles_n,
-    void* __restrict__ out) {
+    void* __restrict__ out, unsigned long long* __restrict__ claims) {
   constexpr int TM = BM / WM, TN = BN / WN, MB = TM / 16, NB = TN / 16;
   static_assert(STAGES == 2 || STAGES == 3, "ring depth");
   using WF = WFormat<F>;
@@ -374,10 +380,24 @@ void ffn_tiled_dma_kernel(
   const int li = lane & 15;
   const int lg = lane >> 4;
 
+  // this workgroup's tile: the next one claimed from the XCD queues (claims
+  // given), else the static order (claim_tile, static_tile)
+  __shared__ int s_tile;
   int e, row0, nrows, nt;
   constexpr int GM_LONG = kGateUp ? 2 * GM : GM;
-  if (!block_tile<BM, GM, GM_LONG>(offsets, E, n_tiles_n, kXcds, xcd_grain(kGateUp, n_tiles_n), e, row0, nrows, nt))
-    return;
+  {
+    const TileGrid g = tile_grid<BM>(offsets, E, n_tiles_n, kXcds, claims ? 1 : xcd_grain(kGateUp, n_tiles_n));
+    int tile;
+    if (claims) {
+      if (tid == 0) s_tile = claim_tile(claims, (int)(blockIdx.x % kXcds), g.per_xcd, g.total);
+      __syncthreads();
+      tile = s_tile;
+    } else {
+      tile = static_tile(g, kXcds);
+    }
+    if (tile < 0) return;
+    decode_tile<BM, GM, GM_LONG>(g, tile, E, n_tiles_n, e, row0, nrows, nt);
+  }
   const int n0 = nt * CH_TILE;
 
   // activation sources: instruction j of this wave covers rows 8*(A_INSTR*wave + j) + lane/8;
@@ -471,15 +491,19 @@ void ffn_tiled_dma_kernel(
     }                                                                                               \
   }
 
-// The MFMAs of one sub-step: every weight fragment converted, then the i-j
-// MFMA nest (the compiler interleaves the two; pinning the interleave with
-// scheduling groups, or converting fragment j right before its MFMAs,
-// measured slower).
+// The MFMAs of one sub-step, weight fragment by weight fragment: fragment j is
+// converted, then its MFMAs over the row blocks, so the first MFMAs wait for
+// one conversion instead of all of them (the compiler interleaves the next
+// fragment's conversion with these MFMAs; each accumulator still receives one
+// MFMA per sub-step, so the sums are unchanged). Against converting every
+// fragment before an i-j nest: Mini prefill gate/up 1-1.5% faster, Large
+// 0.5-1%; pinning the interleave with scheduling groups measured 1-3% slower.
 #define MOE_DMA_MMA(MBV)                                                                            \
-  _Pragma("unroll") for (int j = 0; j < NB; ++j) wf[j] = WF::operand(wq[j], ks);                    \
-  _Pragma("unroll") for (int i = 0; i < MB; ++i)                                                    \
-    if (i < (MBV))                                                                                  \
-      _Pragma("unroll") for (int j = 0; j < NB; ++j) acc[i][j] = mfma_bf16(wf[j], xf[i], acc[i][j]);
+  _Pragma("unroll") for (int j = 0; j < NB; ++j) {                                                  \
+    wf[j] = WF::operand(wq[j], ks);                                                                 \
+    _Pragma("unroll") for (int i = 0; i < MB; ++i)                                                  \
+      if (i < (MBV)) acc[i][j] = mfma_bf16(wf[j], xf[i], acc[i][j]);                                 \
+  }
 
   // per-lane scales of the channels this lane holds in the result, read before
   // the main loop so the epilogue waits on no load: gate/up keeps the gate
@@ -598,6 +622,18 @@ void ffn_tiled_dma_kernel(
   }
 }
 
+__global__ void zero_claims_kernel(unsigned long long* __restrict__ claims) {
+  if (threadIdx.x < kXcds) claims[threadIdx.x] = 0ull;
+}
+
+// Spare blocks of a pass with dynamic tile claims, as a fraction of its most
+// tiles: room for the faster XCDs to take more than their share (Large prefill
+// skewed, A/B on one box: 1/16 measured best, 1/8 and 1/4 slower: more tiles
+// leave the XCD whose queue holds their operands)
+#ifndef MOE_CLAIM_SPARE
+#define MOE_CLAIM_SPARE 16
+#endif
+
 template <bool kGateUp, bool kScaleBf16, int F, int DBN>
 hipError_t launch_dma_pass(const FfnArgs& a, hipStream_t stream) {
   constexpr int GM = kGateUp ? MOE_TILE_GM_GU : MOE_TILE_GM;
@@ -606,16 +642,29 @@ hipError_t launch_dma_pass(const FfnArgs& a, hipStream_t stream) {
   const int N = kGateUp ? a.f : a.d;
   const int Kd = kGateUp ? a.d : a.f;
   const int dn_tiles = (N + DCH - 1) / DCH;
-  const long dblocks = tiled_grid_blocks(kGateUp, (long)(a.S + DBM - 1) / DBM + a.E, dn_tiles);
+  const long m_tiles_max = (long)(a.S + DBM - 1) / DBM + a.E;
+  // dynamic tile claims for the down pass only: on the gate/up pass, whose
+  // tiles are 2-4x shorter, the claim's atomic at every workgroup start cost
+  // more than the balance gained (A/B on one box: Mini prefill gate/up 3%
+  // slower, Large 1% slower; down 0.6-2.7% faster on Large, same on Mini)
+  unsigned long long* claims = kGateUp ? nullptr : a.claims_down;
+  long dblocks;
+  if (claims) {
+    const long total_max = m_tiles_max * dn_tiles;
+    dblocks = (total_max + total_max / MOE_CLAIM_SPARE + kXcds - 1) / kXcds * kXcds;
+    hipLaunchKernelGGL(zero_claims_kernel, dim3(1), dim3(kWave), 0, stream, claims);
+  } else {
+    dblocks = tiled_grid_blocks(kGateUp, m_tiles_max, dn_tiles);
+  }
   const dim3 dblock(DWM * DWN * kWave);
   if constexpr (kGateUp) {
     hipLaunchKernelGGL((ffn_tiled_dma_kernel<true, kScaleBf16, F, GM, DBM, DBN, DWM, DWN, DST>), dim3((unsigned)dblocks),
                        dblock, 0, stream, static_cast<const __bf16*>(a.x), a.sorted_slots, a.K, a.w_gate, a.w_up,
-                       a.s_gate, a.s_up, a.offsets, a.E, N, Kd, dn_tiles, static_cast<void*>(a.h));
+                       a.s_gate, a.s_up, a.offsets, a.E, N, Kd, dn_tiles, static_cast<void*>(a.h), claims);
   } else {
     hipLaunchKernelGGL((ffn_tiled_dma_kernel<false, kScaleBf16, F, GM, DBM, DBN, DWM, DWN, DST>), dim3((unsigned)dblocks),
                        dblock, 0, stream, static_cast<const __bf16*>(a.h), a.sorted_slots, a.K, a.w_down, nullptr,
-                       a.s_down, nullptr, a.offsets, a.E, N, Kd, dn_tiles, static_cast<void*>(a.y_rows));
+                       a.s_down, nullptr, a.offsets, a.E, N, Kd, dn_tiles, static_cast<void*>(a.y_rows), claims);
   }
   return hipGetLastError();
 }

@@ -37,8 +37,14 @@ struct FfnArgs {
   int32_t* perm_offsets;
   int32_t* perm_sorted;
   int32_t* perm_s2r;
+  // tile claim words of the tiled down pass ([8], zeroed by the pass before
+  // use), or null: the static tile order (the gate/up pass always takes it)
+  unsigned long long* claims_down;
   int T, d, f, E, K, S;
 };
+
+// Bytes of the tiled down pass's tile claim words (eight 64-bit words, padded).
+constexpr size_t kTileClaimBytes = 256;
 
 // Weight-streaming schedule for few rows per expert (decode): gate/up pass
 // (x -> h) and down pass (h -> y_rows).

@@ -169,9 +169,11 @@ def moe_expert_down(h: torch.Tensor, expert_offsets: torch.Tensor, experts: Int8
                     y_rows: Optional[torch.Tensor] = None, split_workspace: bool = True,
                     workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Down pass: y_rows [T*K, d] fp32 from h [T*K, f] bf16. With split_workspace the
-    call gets the partial-sum workspace it can use (`workspace` if given, else a new
-    one; none for most shapes); without it a split reduction stays inside one
-    workgroup (same result, bit for bit)."""
+    call gets the workspace it can use (`workspace` if given, else a new one: the
+    stream schedule's partial sums of a split reduction, none for most stream
+    shapes, or the tiled schedule's tile claim words); without it a split
+    reduction stays inside one workgroup and tiles follow the static order (same
+    result, bit for bit)."""
     lib = _lib_handle()
     shape = make_shape(T, experts.d, experts.f, experts.E, K, act, experts.scale_dtype, path, experts.fmt)
     if y_rows is None:

@@ -145,11 +145,11 @@ def test_workspace_holds_split_down_planes(lib):
     # the same with 6 reduction steps (fewer than the split): none
     n, base, _ = sizes(300, 256, 384, 16, 2, 1)
     assert n == base
-    # at most 32 rows per expert (the 32-row variant), or the tiled schedule: none
+    # at most 32 rows per expert (the 32-row variant): none
     n, base, _ = sizes(256, 256, 512, 16, 2, 1)
     assert n == base
     n, base, _ = sizes(300, 256, 512, 16, 2, 2)
-    assert n == base
+    assert n == base + 256              # the tiled schedule: the down pass's tile claim words
 
 
 def test_empty_input_enqueues_nothing(lib):
@@ -196,6 +196,24 @@ def test_quantize_validation(lib):
     assert lib.moe_quantize_rows(4, 64, 1, A, 1, None, A, None) == 1
     assert lib.moe_quantize_rows(4, 64, 1, MIS, 1, A, A, None) == 4
     assert lib.moe_quantize_rows(0, 64, 1, A, 1, A, A, None) == 0
+
+
+def test_tiled_down_pass_takes_tile_claim_words(lib):
+    """On the tiled schedule the down pass can take 256 bytes of tile claim words:
+    moe_forward's and moe_expert_ffn's workspaces hold them, moe_expert_down takes
+    them in its optional workspace (short or misaligned: an error)."""
+    r = lambda v: (v + 255) // 256 * 256
+    T, d, f, E, K = 512, 256, 512, 4, 2
+    S = T * K
+    s = _shape(T=T, d=d, f=f, E=E, K=K, ffn_path=2)
+    n, dn, ff = (ctypes.c_size_t(0) for _ in range(3))
+    assert lib.moe_workspace_size(ctypes.byref(s), ctypes.byref(n)) == 0
+    assert n.value == 4 * r(S * 4) + r((E + 1) * 4) + r(S * f * 2) + r(S * d * 4) + 256
+    assert lib.moe_down_workspace_size(ctypes.byref(s), ctypes.byref(dn)) == 0 and dn.value == 256
+    assert lib.moe_ffn_workspace_size(ctypes.byref(s), ctypes.byref(ff)) == 0
+    assert ff.value == r(S * f * 2) + 256
+    assert lib.moe_expert_down(ctypes.byref(s), A, A, A, A, A, A, ctypes.c_size_t(255), None) == 5
+    assert lib.moe_expert_down(ctypes.byref(s), A, A, A, A, A, MIS, ctypes.c_size_t(256), None) == 4
 
 
 def test_weight_format_rules(lib):

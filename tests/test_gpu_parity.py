@@ -9,8 +9,8 @@ import pytest
 import torch
 
 import workloads
-from int8_weight_moe_amd import (MoeError, moe_combine, moe_expert_ffn, moe_forward, moe_mlp_forward, moe_pack_rows,
-                                 moe_permute, moe_quantize_rows, moe_route)
+from int8_weight_moe_amd import (MoeError, moe_combine, moe_expert_down, moe_expert_ffn, moe_expert_gate_up, moe_forward,
+                                 moe_mlp_forward, moe_pack_rows, moe_permute, moe_quantize_rows, moe_route)
 from int8_weight_moe_amd._lib import MOE_PATH_AUTO, MOE_PATH_STREAM, MOE_PATH_TILED
 from oracle import moe as omoe
 from oracle import quant as oquant
@@ -209,6 +209,34 @@ def test_long_and_short_experts_in_one_launch(path):
     assert_close_to_oracle(np64(rows), o.reshape(T * K, -1)[ss.cpu().numpy()], "y_rows (every row)")
     ref = omoe.moe_forward(x64, wr64, b64, W, K, ids=ids_g)["y"]
     assert_close_to_oracle(np64(y), ref, "y (every token)")
+
+
+@pytest.mark.parametrize("T,d,f,E,K,bias", [
+    (4000, 192, 320, 4, 2, [8.0, 0.0, 0.0, 0.0]),    # one long expert, short ones, ragged tiles
+    (8000, 128, 1024, 8, 2, None),                   # more tiles than the GPU holds at once
+    (600, 256, 384, 16, 2, None),
+])
+def test_down_tile_claims_equal_static_order_bitwise(T, d, f, E, K, bias):
+    """The tiled down pass with tile claim words (workgroups take tiles from XCD
+    queues with atomic claims) and without (tile fixed by the workgroup id)
+    computes every tile the same way: y_rows is identical bit for bit, twice in
+    a row on the same claim words, and matches the oracle."""
+    w, x, wr, b, W = _case(T, d, f, E, K, "bf16", "bf16", bias=bias, seed=31)
+    ex = experts_to_device(W, torch.bfloat16)
+    xg = x.cuda()
+    ids, _ = moe_route(xg, wr.cuda(), None if b is None else b.cuda(), K)
+    off, ss, s2r = moe_permute(ids, E)
+    h = moe_expert_gate_up(xg, off, ss, ex, K, path=MOE_PATH_TILED)
+    ws = torch.empty(256, dtype=torch.uint8, device="cuda")
+    r_dyn = moe_expert_down(h, off, ex, T, K, path=MOE_PATH_TILED, workspace=ws)
+    r_sta = moe_expert_down(h, off, ex, T, K, path=MOE_PATH_TILED, split_workspace=False)
+    r_dyn2 = moe_expert_down(h, off, ex, T, K, path=MOE_PATH_TILED, workspace=ws)   # claim words reused: cleared by the pass
+    torch.cuda.synchronize()
+    assert torch.equal(r_dyn, r_sta) and torch.equal(r_dyn, r_dyn2)
+    ids_h = ids.cpu().numpy()
+    o = omoe.expert_outputs(np64(x), ids_h, W)
+    assert_close_to_oracle(np64(r_dyn), o.reshape(T * K, -1)[ss.cpu().numpy()], "y_rows with tile claims")
+    del h
 
 
 def test_tiled_register_staged_bf16_past_32bit_offsets():
