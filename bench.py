@@ -178,7 +178,7 @@ def time_stages(layer, x, path, steps, warmup, dense=False):
     the combine are timed."""
     import torch
     from int8_weight_moe_amd import moe_combine, moe_expert_down, moe_expert_gate_up, moe_permute, moe_route
-    from int8_weight_moe_amd.ops import down_workspace_size, make_shape
+    from int8_weight_moe_amd.ops import down_workspace_size, gate_up_workspace_size, make_shape
     ex, K = layer.experts, layer.K
     T = x.shape[0]
     names = ["gate_up", "down", "combine"] if dense else ["route", "permute", "gate_up", "down", "combine"]
@@ -186,6 +186,7 @@ def time_stages(layer, x, path, steps, warmup, dense=False):
     rows = torch.empty((T * K, ex.d), dtype=torch.float32, device=x.device)
     dshape = make_shape(T, ex.d, ex.f, ex.E, K, x.dtype, ex.scale_dtype, path, ex.fmt)
     dws = torch.empty(max(down_workspace_size(dshape), 256), dtype=torch.uint8, device=x.device)
+    gws = torch.empty(max(gate_up_workspace_size(dshape), 256), dtype=torch.uint8, device=x.device)
     if dense:
         ids0, gw0 = moe_route(x, layer.router_w, layer.bias, K)
         layout = (gw0,) + tuple(moe_permute(ids0, ex.E))
@@ -202,7 +203,7 @@ def time_stages(layer, x, path, steps, warmup, dense=False):
             off, ss, s2r = moe_permute(ids, ex.E)
             i += 1
             ev[i].record()
-        moe_expert_gate_up(x, off, ss, ex, K, path=path, h=h)
+        moe_expert_gate_up(x, off, ss, ex, K, path=path, h=h, workspace=gws)
         ev[i + 1].record()
         moe_expert_down(h, off, ex, T, K, act=x.dtype, path=path, y_rows=rows, workspace=dws)
         ev[i + 2].record()

@@ -113,12 +113,13 @@ const char* moe_status_str(moe_status status);
 const char* moe_last_error(void);
 
 /* Workspace, in bytes, that moe_forward needs for this shape (includes the
- * routing buffers, the permutation, h, y_rows and the down pass's own
- * workspace, see moe_down_workspace_size). */
+ * routing buffers, the permutation, h, y_rows and the FFN passes' own
+ * workspaces, see moe_gate_up_workspace_size and moe_down_workspace_size). */
 moe_status moe_workspace_size(const moe_shape* shape, size_t* bytes);
 
 /* Workspace, in bytes, that moe_expert_ffn needs: h (T*K*f bf16), then the
- * down pass's workspace (moe_down_workspace_size), each padded to 256. */
+ * down pass's workspace (moe_down_workspace_size), then the gate/up pass's
+ * (moe_gate_up_workspace_size), each padded to 256. */
 moe_status moe_ffn_workspace_size(const moe_shape* shape, size_t* bytes);
 
 /* Workspace, in bytes, that the down pass can use:
@@ -128,6 +129,10 @@ moe_status moe_ffn_workspace_size(const moe_shape* shape, size_t* bytes);
  *     the GPU, e.g. a dense MLP at decode); 0 for every other stream shape;
  *   - TILED schedule: 256 bytes of tile claim words (see moe_expert_down). */
 moe_status moe_down_workspace_size(const moe_shape* shape, size_t* bytes);
+
+/* Workspace, in bytes, that the gate/up pass can use: 256 bytes of tile claim
+ * words on the TILED schedule, 0 on the STREAM schedule (see moe_expert_gate_up). */
+moe_status moe_gate_up_workspace_size(const moe_shape* shape, size_t* bytes);
 
 /* Router and gate (paper: "Model Architecture", top K of n experts per token).
  *   x           [T, d]  act_dtype
@@ -178,23 +183,26 @@ moe_status moe_expert_ffn(const moe_shape* shape, const void* x,
  * gate/up  h[r] = silu(s_g * (q_g . x_r)) * (s_u * (q_u . x_r))  for every sorted row r,
  *          h [T*K, f] bf16 out (rows past off[E] untouched).
  * down     y_rows[r] = s_d * (q_d . h[r]),  h [T*K, f] bf16 in, y_rows [T*K, d] fp32 out.
- *          workspace: NULL, or 16-byte aligned and at least
- *          moe_down_workspace_size bytes (else MOE_ERR_ALIGN /
- *          MOE_ERR_WORKSPACE). Its contents need not be initialised. With it:
- *          - on the TILED schedule, the pass's workgroups claim their tiles
- *            through atomic counters in the workspace (cleared by the pass
- *            itself) and XCDs that run faster take more tiles; without it
- *            every workgroup's tile is fixed by its id;
+ * workspace (both passes): NULL, or 16-byte aligned and at least
+ *          moe_gate_up_workspace_size / moe_down_workspace_size bytes (else
+ *          MOE_ERR_ALIGN / MOE_ERR_WORKSPACE). Its contents need not be
+ *          initialised. With it:
+ *          - on the TILED schedule, the last tiles of each XCD's share are
+ *            claimed through atomic counters in the workspace (cleared by the
+ *            pass itself) by the workgroups of any XCD, so XCDs that run
+ *            faster take more tiles; without it every workgroup's tile is
+ *            fixed by its id;
  *          - on the STREAM schedule, a down pass that splits its reduction
  *            may spread the slices over workgroups (partial sums in the
  *            workspace, added in slice order by a second kernel); without it
  *            the slices stay inside one workgroup.
  *          The results are the same bit for bit either way.
  * moe_expert_ffn is moe_expert_gate_up followed by moe_expert_down on the same
- * stream, with the part of its workspace after h as the down workspace. */
+ * stream, with the parts of its workspace after h as their workspaces. */
 moe_status moe_expert_gate_up(const moe_shape* shape, const void* x, const int32_t* expert_offsets,
                               const int32_t* sorted_slots, const void* w_gate, const void* w_up,
-                              const void* s_gate, const void* s_up, void* h, hipStream_t stream);
+                              const void* s_gate, const void* s_up, void* h, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream);
 moe_status moe_expert_down(const moe_shape* shape, const void* h, const int32_t* expert_offsets,
                            const void* w_down, const void* s_down, float* y_rows, void* workspace,
                            size_t workspace_bytes, hipStream_t stream);

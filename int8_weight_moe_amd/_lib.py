@@ -26,7 +26,7 @@ EXPORTS = (
     "moe_abi_version", "moe_status_str", "moe_last_error", "moe_workspace_size", "moe_ffn_workspace_size",
     "moe_route", "moe_permute", "moe_expert_ffn", "moe_expert_gate_up", "moe_expert_down", "moe_combine", "moe_forward", "moe_quantize_rows",
     "moe_pack_rows", "moe_mlp_workspace_size", "moe_mlp_forward", "moe_quantize_rows_fp8", "moe_down_workspace_size",
-    "moe_forward_noalloc",
+    "moe_forward_noalloc", "moe_gate_up_workspace_size",
 )
 
 
@@ -53,7 +53,8 @@ _SIGS = {
     "moe_route": (ctypes.c_int32, [_SHAPE, _P, _P, _P, _P, _P, _P]),
     "moe_permute": (ctypes.c_int32, [_SHAPE, _P, _P, _P, _P, _P]),
     "moe_expert_ffn": (ctypes.c_int32, [_SHAPE, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
-    "moe_expert_gate_up": (ctypes.c_int32, [_SHAPE, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "moe_expert_gate_up": (ctypes.c_int32, [_SHAPE, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "moe_gate_up_workspace_size": (ctypes.c_int32, [_SHAPE, ctypes.POINTER(ctypes.c_size_t)]),
     "moe_expert_down": (ctypes.c_int32, [_SHAPE, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "moe_down_workspace_size": (ctypes.c_int32, [_SHAPE, ctypes.POINTER(ctypes.c_size_t)]),
     "moe_combine": (ctypes.c_int32, [_SHAPE, _P, _P, _P, _P, _P]),

@@ -83,8 +83,8 @@ WsLayout forward_layout(const moe_shape* s) {
   // partial sums of a stream down pass split over workgroups (none otherwise)
   L.part_bytes = use_stream(s) ? down_ws_bytes(s) : 0;
   L.part = o;    o += round_up(L.part_bytes);
-  // tile claim words of the tiled down pass (none for the stream schedule)
-  L.claims = o;  o += use_stream(s) ? 0 : moe::kTileClaimBytes;
+  // tile claim words of the tiled gate/up and down passes (none for the stream schedule)
+  L.claims = o;  o += use_stream(s) ? 0 : 2 * moe::kTileClaimBytes;
   L.total = o;
   return L;
 }
@@ -99,9 +99,14 @@ size_t down_ws_bytes(const moe_shape* s) {
   return (size_t)planes * (size_t)S * (size_t)s->d * 4;
 }
 
-// moe_expert_ffn: h, then the down pass's workspace
+// Workspace of the gate/up pass: the tiled schedule's tile claim words.
+size_t gate_up_ws_bytes(const moe_shape* s) { return use_stream(s) ? 0 : moe::kTileClaimBytes; }
+
+// moe_expert_ffn: h, then the down pass's workspace, then the gate/up pass's
 size_t ffn_h_bytes(const moe_shape* s) { return round_up((size_t)s->T * s->K * (size_t)s->f * 2); }
-size_t ffn_ws_bytes(const moe_shape* s) { return ffn_h_bytes(s) + round_up(down_ws_bytes(s)); }
+size_t ffn_ws_bytes(const moe_shape* s) {
+  return ffn_h_bytes(s) + round_up(down_ws_bytes(s)) + round_up(gate_up_ws_bytes(s));
+}
 
 bool use_stream(const moe_shape* s) {
   if (s->ffn_path == MOE_PATH_STREAM) return true;
@@ -143,7 +148,7 @@ moe::FfnArgs ffn_args(const moe_shape* s, const void* x, const int32_t* offsets,
   a.part = nullptr;
   a.ids = nullptr;
   a.perm_offsets = a.perm_sorted = a.perm_s2r = nullptr;
-  a.claims_down = nullptr;
+  a.claims_gate_up = a.claims_down = nullptr;
   a.T = s->T;
   a.d = s->d;
   a.f = s->f;
@@ -251,7 +256,10 @@ moe_status forward_impl(const moe_shape* s, const void* x, const void* router_w,
   if (e != hipSuccess) return hip_fail(e, "router launch");
   moe::FfnArgs a = ffn_args(s, x, offsets, sorted, w_gate, w_up, w_down, s_gate, s_up, s_down, y_rows, h);
   if (L.part_bytes) a.part = reinterpret_cast<float*>(ws + L.part);
-  if (!use_stream(s)) a.claims_down = reinterpret_cast<unsigned long long*>(ws + L.claims);
+  if (!use_stream(s)) {
+    a.claims_gate_up = reinterpret_cast<unsigned long long*>(ws + L.claims);
+    a.claims_down = reinterpret_cast<unsigned long long*>(ws + L.claims + moe::kTileClaimBytes);
+  }
   if (use_stream(s) && moe::stream_gate_up_takes_ids((long)s->T * s->K, s->E)) {
     // at most 256 slots: the gate/up pass derives the permutation from the ids
     // and writes it for the down pass and the combine (one launch fewer)
@@ -373,6 +381,7 @@ moe_status moe_expert_ffn(const moe_shape* s, const void* x, const int32_t* expe
     if (down_ws_bytes(s)) a.part = reinterpret_cast<float*>(dws);
   } else {
     a.claims_down = reinterpret_cast<unsigned long long*>(dws);
+    a.claims_gate_up = reinterpret_cast<unsigned long long*>(dws + round_up(down_ws_bytes(s)));
   }
   st = run_gate_up(s, a, stream);
   if (st != MOE_OK) return st;
@@ -381,7 +390,8 @@ moe_status moe_expert_ffn(const moe_shape* s, const void* x, const int32_t* expe
 
 moe_status moe_expert_gate_up(const moe_shape* s, const void* x, const int32_t* expert_offsets,
                               const int32_t* sorted_slots, const void* w_gate, const void* w_up,
-                              const void* s_gate, const void* s_up, void* h, hipStream_t stream) {
+                              const void* s_gate, const void* s_up, void* h, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream) {
   moe_status st = check_shape(s);
   if (st != MOE_OK) return st;
   st = check_ffn(s);
@@ -395,8 +405,15 @@ moe_status moe_expert_gate_up(const moe_shape* s, const void* x, const int32_t* 
   REQUIRE_SCALE(s, s_gate);
   REQUIRE_SCALE(s, s_up);
   REQUIRE_PTR(h);
-  const moe::FfnArgs a = ffn_args(s, x, expert_offsets, sorted_slots, w_gate, w_up, nullptr, s_gate, s_up, nullptr,
-                                  nullptr, static_cast<__bf16*>(h));
+  const size_t need = gate_up_ws_bytes(s);
+  if (workspace) {
+    if (!aligned16(workspace)) return fail(MOE_ERR_ALIGN, "workspace is not 16-byte aligned");
+    if (workspace_bytes < need)
+      return fail(MOE_ERR_WORKSPACE, "workspace_bytes=%zu < required %zu", workspace_bytes, need);
+  }
+  moe::FfnArgs a = ffn_args(s, x, expert_offsets, sorted_slots, w_gate, w_up, nullptr, s_gate, s_up, nullptr,
+                            nullptr, static_cast<__bf16*>(h));
+  if (workspace && need) a.claims_gate_up = static_cast<unsigned long long*>(workspace);
   return run_gate_up(s, a, stream);
 }
 
@@ -436,6 +453,14 @@ moe_status moe_down_workspace_size(const moe_shape* shape, size_t* bytes) {
   if (st != MOE_OK) return st;
   if (!bytes) return fail(MOE_ERR_NULL, "bytes is NULL");
   *bytes = down_ws_bytes(shape);
+  return MOE_OK;
+}
+
+moe_status moe_gate_up_workspace_size(const moe_shape* shape, size_t* bytes) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (!bytes) return fail(MOE_ERR_NULL, "bytes is NULL");
+  *bytes = gate_up_ws_bytes(shape);
   return MOE_OK;
 }
 
@@ -521,7 +546,10 @@ moe_status moe_mlp_forward(const moe_shape* s, const void* x, const void* w_gate
   if (e != hipSuccess) return hip_fail(e, "dense init launch");
   moe::FfnArgs a = ffn_args(s, x, offsets, sorted, w_gate, w_up, w_down, s_gate, s_up, s_down, y_rows, h);
   if (L.part_bytes) a.part = reinterpret_cast<float*>(ws + L.part);
-  if (!use_stream(s)) a.claims_down = reinterpret_cast<unsigned long long*>(ws + L.claims);
+  if (!use_stream(s)) {
+    a.claims_gate_up = reinterpret_cast<unsigned long long*>(ws + L.claims);
+    a.claims_down = reinterpret_cast<unsigned long long*>(ws + L.claims + moe::kTileClaimBytes);
+  }
   st = run_gate_up(s, a, stream);
   if (st != MOE_OK) return st;
   st = run_down(s, a, stream);

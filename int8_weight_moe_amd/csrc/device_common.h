@@ -167,24 +167,39 @@ __device__ __forceinline__ int static_tile(const TileGrid& g, int xcds) {
   return tile < g.total ? tile : -1;
 }
 
-// Dynamic tile order (load balance across XCDs that run at different speeds):
-// a workgroup claims the next tile of its XCD's queue with one atomic
-// increment of claims[x], and once that queue is empty the next tile of the
-// other queues in turn. Every tile is claimed exactly once (each claim sees
-// the claims before it) as long as the grid has a block per tile; the grid
-// carries spare blocks so that faster XCDs can take more than their share,
-// and blocks that find every queue empty exit. claims[0..7] start at zero.
-// One lane calls it; -1 when every queue is empty.
-__device__ __forceinline__ int claim_tile(unsigned long long* __restrict__ claims, int x_home, int per_xcd,
-                                          int total) {
-  for (int i = 0; i < 8; ++i) {
-    const int x = (x_home + i) & 7;
-    const int len = min(per_xcd, total - x * per_xcd);
-    if (len <= 0) continue;
-    const int k = (int)atomicAdd(&claims[x], 1ull);
-    if (k < len) return x * per_xcd + k;
+// Claimed tail (load balance across XCDs that run at different speeds, and a
+// less ragged end of the pass): the first len - P tiles of each XCD queue go
+// statically to the workgroups of that XCD (block b takes tile
+// x*per_xcd + b/xcds, x = b % xcds, for b/xcds < per_xcd - P), and the last P
+// tiles of each queue form its tail, which the later blocks claim with one
+// atomic increment of claims[x]: their own XCD's tail first, then the others'
+// in turn, so an XCD that runs faster takes part of the slower ones' tails.
+// Only the tail blocks pay for an atomic. Every tile is claimed exactly once
+// (each claim sees the claims before it) as long as the tail blocks outnumber
+// the tail tiles; blocks that find every tail claimed exit. claims[0..7] start
+// at zero.
+// Returns -1 for blocks without a tile. All threads of the block call it.
+__device__ __forceinline__ int claimed_tail_tile(const TileGrid& g, int xcds, int P,
+                                                 unsigned long long* __restrict__ claims, int* s_tile) {
+  const int x = blockIdx.x % xcds, k = blockIdx.x / xcds;
+  const int pre = max(0, g.per_xcd - P);   // static tiles of a full queue
+  if (k < pre) {
+    const int len = min(g.per_xcd, g.total - x * g.per_xcd);
+    return k < len ? x * g.per_xcd + k : -1;
   }
-  return -1;
+  if (threadIdx.x == 0) {
+    int t = -1;
+    for (int i = 0; i < xcds && t < 0; ++i) {
+      const int y = (x + i) % xcds;
+      const int tail = min(g.per_xcd, g.total - y * g.per_xcd) - pre;
+      if (tail <= 0) continue;
+      const int j = (int)atomicAdd(&claims[y], 1ull);
+      if (j < tail) t = y * g.per_xcd + pre + j;
+    }
+    *s_tile = t;
+  }
+  __syncthreads();
+  return *s_tile;
 }
 
 // Tile of this workgroup in the static order (the decode of static_tile).

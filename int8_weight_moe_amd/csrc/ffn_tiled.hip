@@ -26,13 +26,11 @@
 // inside a group, so the tiles that run together share a few activation tiles
 // and weight tiles of one expert. That order is cut into 8 contiguous XCD
 // queues of equal length (workgroups are dealt round-robin to the 8 XCDs), so
-// each XCD keeps its operands in its own L2. With tile claim words (the down
-// pass's workspace), each workgroup of the direct-to-LDS kernel claims the next tile
-// of its XCD's queue with an atomic increment, and takes the next tile of
-// another queue once its own is empty: XCDs that run faster (the same tiles
-// took up to 5% longer on some XCDs than on others) then take more tiles.
-// Without them (and always on the gate/up pass), workgroup ids map to the
-// queues statically.
+// each XCD keeps its operands in its own L2. Workgroup ids map to the queues
+// statically; with tile claim words (a workspace), the last tiles of each
+// queue are claimed with atomics instead, by the later workgroups of any XCD,
+// so XCDs that run faster (the same tiles took up to 5% longer on some XCDs
+// than on others) take part of the slower ones' tails.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -43,6 +41,15 @@ namespace {
 constexpr int kBK = 64;      // reduction step (elements)
 constexpr int kChunks = kBK / 8;  // 16-byte bf16 chunks per LDS row
 constexpr int kXcds = 8;
+
+// Tiles at the end of each XCD queue that are claimed instead of assigned
+// statically (about two rounds of the XCD's 64 workgroup slots). A/B on one box
+// against the static order: Large prefill skewed gate/up 2.1% and down 2.6%
+// faster with 128 (256: the same; 64: 0.6% and 2.2%), Mini prefill 0.6-1.2%;
+// claiming every tile instead cost gate/up 1-3% (an atomic at every
+// workgroup start) and, with thieves taking the front of other queues, L2
+// locality.
+constexpr int kClaimTail = 128;
 
 // Granularity of the XCD shares of a pass's tiles. Gate/up: exact shares
 // (balanced to a tile). Down: whole multiples of the channel-tile count, which
@@ -380,8 +387,8 @@ void ffn_tiled_dma_kernel(
   const int li = lane & 15;
   const int lg = lane >> 4;
 
-  // this workgroup's tile: the next one claimed from the XCD queues (claims
-  // given), else the static order (claim_tile, static_tile)
+  // this workgroup's tile: the static order with claimed queue tails (claims
+  // given), else the static order throughout (claimed_tail_tile, static_tile)
   __shared__ int s_tile;
   int e, row0, nrows, nt;
   constexpr int GM_LONG = kGateUp ? 2 * GM : GM;
@@ -389,9 +396,7 @@ void ffn_tiled_dma_kernel(
     const TileGrid g = tile_grid<BM>(offsets, E, n_tiles_n, kXcds, claims ? 1 : xcd_grain(kGateUp, n_tiles_n));
     int tile;
     if (claims) {
-      if (tid == 0) s_tile = claim_tile(claims, (int)(blockIdx.x % kXcds), g.per_xcd, g.total);
-      __syncthreads();
-      tile = s_tile;
+      tile = claimed_tail_tile(g, kXcds, kClaimTail, claims, &s_tile);
     } else {
       tile = static_tile(g, kXcds);
     }
@@ -626,13 +631,6 @@ __global__ void zero_claims_kernel(unsigned long long* __restrict__ claims) {
   if (threadIdx.x < kXcds) claims[threadIdx.x] = 0ull;
 }
 
-// Spare blocks of a pass with dynamic tile claims, as a fraction of its most
-// tiles: room for the faster XCDs to take more than their share (Large prefill
-// skewed, A/B on one box: 1/16 measured best, 1/8 and 1/4 slower: more tiles
-// leave the XCD whose queue holds their operands)
-#ifndef MOE_CLAIM_SPARE
-#define MOE_CLAIM_SPARE 16
-#endif
 
 template <bool kGateUp, bool kScaleBf16, int F, int DBN>
 hipError_t launch_dma_pass(const FfnArgs& a, hipStream_t stream) {
@@ -643,15 +641,13 @@ hipError_t launch_dma_pass(const FfnArgs& a, hipStream_t stream) {
   const int Kd = kGateUp ? a.d : a.f;
   const int dn_tiles = (N + DCH - 1) / DCH;
   const long m_tiles_max = (long)(a.S + DBM - 1) / DBM + a.E;
-  // dynamic tile claims for the down pass only: on the gate/up pass, whose
-  // tiles are 2-4x shorter, the claim's atomic at every workgroup start cost
-  // more than the balance gained (A/B on one box: Mini prefill gate/up 3%
-  // slower, Large 1% slower; down 0.6-2.7% faster on Large, same on Mini)
-  unsigned long long* claims = kGateUp ? nullptr : a.claims_down;
+  unsigned long long* claims = kGateUp ? a.claims_gate_up : a.claims_down;
   long dblocks;
   if (claims) {
-    const long total_max = m_tiles_max * dn_tiles;
-    dblocks = (total_max + total_max / MOE_CLAIM_SPARE + kXcds - 1) / kXcds * kXcds;
+    // the static blocks of the longest queue, then one and a half times its tail
+    const long per_xcd_max = (m_tiles_max * dn_tiles + kXcds - 1) / kXcds;
+    const long tail = min(per_xcd_max, (long)kClaimTail);
+    dblocks = kXcds * (per_xcd_max + tail / 2);
     hipLaunchKernelGGL(zero_claims_kernel, dim3(1), dim3(kWave), 0, stream, claims);
   } else {
     dblocks = tiled_grid_blocks(kGateUp, m_tiles_max, dn_tiles);

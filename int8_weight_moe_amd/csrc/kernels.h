@@ -37,13 +37,14 @@ struct FfnArgs {
   int32_t* perm_offsets;
   int32_t* perm_sorted;
   int32_t* perm_s2r;
-  // tile claim words of the tiled down pass ([8], zeroed by the pass before
-  // use), or null: the static tile order (the gate/up pass always takes it)
+  // tile claim words of the tiled gate/up and down passes ([8] each, zeroed by
+  // the pass before use), or null: the static tile order throughout
+  unsigned long long* claims_gate_up;
   unsigned long long* claims_down;
   int T, d, f, E, K, S;
 };
 
-// Bytes of the tiled down pass's tile claim words (eight 64-bit words, padded).
+// Bytes of one tiled pass's tile claim words (eight 64-bit words, padded).
 constexpr size_t kTileClaimBytes = 256;
 
 // Weight-streaming schedule for few rows per expert (decode): gate/up pass

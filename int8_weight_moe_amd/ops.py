@@ -142,18 +142,34 @@ def moe_expert_ffn(x: torch.Tensor, expert_offsets: torch.Tensor, sorted_slots: 
     return y_rows
 
 
+def gate_up_workspace_size(shape: MoeShape) -> int:
+    lib = _lib_handle()
+    n = ctypes.c_size_t(0)
+    _lib.check(lib.moe_gate_up_workspace_size(ctypes.byref(shape), ctypes.byref(n)))
+    return n.value
+
+
 def moe_expert_gate_up(x: torch.Tensor, expert_offsets: torch.Tensor, sorted_slots: torch.Tensor,
                        experts: Int8Experts, K: int, path: int = MOE_PATH_AUTO,
-                       h: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Gate/up pass: h [T*K, f] bf16 (sorted-row order)."""
+                       h: Optional[torch.Tensor] = None, use_workspace: bool = True,
+                       workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Gate/up pass: h [T*K, f] bf16 (sorted-row order). With use_workspace the call
+    gets the workspace it can use (`workspace` if given, else a new one: the tiled
+    schedule's tile claim words); without it every tile follows the static order
+    (same result, bit for bit)."""
     lib = _lib_handle()
     T, d = x.shape
     shape = make_shape(T, d, experts.f, experts.E, K, x.dtype, experts.scale_dtype, path, experts.fmt)
     if h is None:
         h = torch.empty((T * K, experts.f), dtype=torch.bfloat16, device=x.device)
+    ws = None
+    need = gate_up_workspace_size(shape) if use_workspace else 0
+    if need:
+        ws = workspace if workspace is not None else torch.empty(need, dtype=torch.uint8, device=x.device)
     _lib.check(lib.moe_expert_gate_up(
         ctypes.byref(shape), _ptr(x), _ptr(expert_offsets), _ptr(sorted_slots), _ptr(experts.q_gate),
-        _ptr(experts.q_up), _ptr(experts.s_gate), _ptr(experts.s_up), _ptr(h), _stream()))
+        _ptr(experts.q_up), _ptr(experts.s_gate), _ptr(experts.s_up), _ptr(h), _ptr(ws),
+        ctypes.c_size_t(ws.numel() if ws is not None else 0), _stream()))
     return h
 
 

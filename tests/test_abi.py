@@ -149,7 +149,7 @@ def test_workspace_holds_split_down_planes(lib):
     n, base, _ = sizes(256, 256, 512, 16, 2, 1)
     assert n == base
     n, base, _ = sizes(300, 256, 512, 16, 2, 2)
-    assert n == base + 256              # the tiled schedule: the down pass's tile claim words
+    assert n == base + 2 * 256          # the tiled schedule: tile claim words of both passes
 
 
 def test_empty_input_enqueues_nothing(lib):
@@ -198,22 +198,28 @@ def test_quantize_validation(lib):
     assert lib.moe_quantize_rows(0, 64, 1, A, 1, A, A, None) == 0
 
 
-def test_tiled_down_pass_takes_tile_claim_words(lib):
-    """On the tiled schedule the down pass can take 256 bytes of tile claim words:
-    moe_forward's and moe_expert_ffn's workspaces hold them, moe_expert_down takes
-    them in its optional workspace (short or misaligned: an error)."""
+def test_tiled_passes_take_tile_claim_words(lib):
+    """On the tiled schedule each FFN pass can take 256 bytes of tile claim words:
+    moe_forward's and moe_expert_ffn's workspaces hold both, the staged passes
+    take them in their optional workspace (short or misaligned: an error)."""
     r = lambda v: (v + 255) // 256 * 256
     T, d, f, E, K = 512, 256, 512, 4, 2
     S = T * K
     s = _shape(T=T, d=d, f=f, E=E, K=K, ffn_path=2)
-    n, dn, ff = (ctypes.c_size_t(0) for _ in range(3))
+    n, g, dn, ff = (ctypes.c_size_t(0) for _ in range(4))
     assert lib.moe_workspace_size(ctypes.byref(s), ctypes.byref(n)) == 0
-    assert n.value == 4 * r(S * 4) + r((E + 1) * 4) + r(S * f * 2) + r(S * d * 4) + 256
+    assert n.value == 4 * r(S * 4) + r((E + 1) * 4) + r(S * f * 2) + r(S * d * 4) + 2 * 256
+    assert lib.moe_gate_up_workspace_size(ctypes.byref(s), ctypes.byref(g)) == 0 and g.value == 256
     assert lib.moe_down_workspace_size(ctypes.byref(s), ctypes.byref(dn)) == 0 and dn.value == 256
     assert lib.moe_ffn_workspace_size(ctypes.byref(s), ctypes.byref(ff)) == 0
-    assert ff.value == r(S * f * 2) + 256
+    assert ff.value == r(S * f * 2) + 256 + 256
+    assert lib.moe_expert_gate_up(ctypes.byref(s), A, A, A, A, A, A, A, A, A, ctypes.c_size_t(255), None) == 5
+    assert lib.moe_expert_gate_up(ctypes.byref(s), A, A, A, A, A, A, A, A, MIS, ctypes.c_size_t(256), None) == 4
     assert lib.moe_expert_down(ctypes.byref(s), A, A, A, A, A, A, ctypes.c_size_t(255), None) == 5
     assert lib.moe_expert_down(ctypes.byref(s), A, A, A, A, A, MIS, ctypes.c_size_t(256), None) == 4
+    # the stream schedule's gate/up pass takes none
+    s = _shape(T=8, ffn_path=1)
+    assert lib.moe_gate_up_workspace_size(ctypes.byref(s), ctypes.byref(g)) == 0 and g.value == 0
 
 
 def test_weight_format_rules(lib):

@@ -216,22 +216,27 @@ def test_long_and_short_experts_in_one_launch(path):
     (8000, 128, 1024, 8, 2, None),                   # more tiles than the GPU holds at once
     (600, 256, 384, 16, 2, None),
 ])
-def test_down_tile_claims_equal_static_order_bitwise(T, d, f, E, K, bias):
-    """The tiled down pass with tile claim words (workgroups take tiles from XCD
-    queues with atomic claims) and without (tile fixed by the workgroup id)
-    computes every tile the same way: y_rows is identical bit for bit, twice in
-    a row on the same claim words, and matches the oracle."""
+def test_tile_claims_equal_static_order_bitwise(T, d, f, E, K, bias):
+    """The tiled passes with tile claim words (the tails of the XCD queues are
+    claimed with atomics) and without (every tile fixed by the workgroup id)
+    compute every tile the same way: h and y_rows are identical bit for bit,
+    also twice in a row on the same claim words, and match the oracle. The
+    second shape has more tiles than the GPU holds at once, so tails are
+    claimed across XCDs."""
     w, x, wr, b, W = _case(T, d, f, E, K, "bf16", "bf16", bias=bias, seed=31)
     ex = experts_to_device(W, torch.bfloat16)
     xg = x.cuda()
     ids, _ = moe_route(xg, wr.cuda(), None if b is None else b.cuda(), K)
     off, ss, s2r = moe_permute(ids, E)
-    h = moe_expert_gate_up(xg, off, ss, ex, K, path=MOE_PATH_TILED)
     ws = torch.empty(256, dtype=torch.uint8, device="cuda")
+    h = moe_expert_gate_up(xg, off, ss, ex, K, path=MOE_PATH_TILED, workspace=ws)
+    h_sta = moe_expert_gate_up(xg, off, ss, ex, K, path=MOE_PATH_TILED, use_workspace=False)
+    h2 = moe_expert_gate_up(xg, off, ss, ex, K, path=MOE_PATH_TILED, workspace=ws)   # claim words reused: cleared by the pass
     r_dyn = moe_expert_down(h, off, ex, T, K, path=MOE_PATH_TILED, workspace=ws)
     r_sta = moe_expert_down(h, off, ex, T, K, path=MOE_PATH_TILED, split_workspace=False)
-    r_dyn2 = moe_expert_down(h, off, ex, T, K, path=MOE_PATH_TILED, workspace=ws)   # claim words reused: cleared by the pass
+    r_dyn2 = moe_expert_down(h, off, ex, T, K, path=MOE_PATH_TILED, workspace=ws)
     torch.cuda.synchronize()
+    assert torch.equal(h.view(torch.int16), h_sta.view(torch.int16)) and torch.equal(h.view(torch.int16), h2.view(torch.int16))
     assert torch.equal(r_dyn, r_sta) and torch.equal(r_dyn, r_dyn2)
     ids_h = ids.cpu().numpy()
     o = omoe.expert_outputs(np64(x), ids_h, W)
