@@ -89,11 +89,16 @@ long tiled_grid_blocks(bool gate_up, long m_tiles_max, int n_tiles_n) {
 // times (Mini prefill gate/up, interleaved A/B on one box: groups of 8
 // 3321-3333 us, of 6 3361-3369, of 4 3434-3466; on another 3336-3341 against
 // 3444-3512; dense MLP prefill 0.5-1.5% faster, Large skewed within 0.5%);
-// the down pass keeps 4 (8 measured 2% slower on Large skewed). An expert with
-// at least 3*8 row tiles takes gate/up groups of up to 16 (Large skewed's two
-// hot experts, 52 row tiles: gate/up 0.5-1% faster, its TP8 share 0.7%)
+// the down pass keeps 4 (8 measured 1-2% slower on Large skewed, 2 6%). An
+// expert with at least 3*8 row tiles takes gate/up groups of up to 12 (Large
+// skewed's two hot experts, 52 row tiles, in 5 groups: with the claimed queue
+// tails, gate/up 0.9-1.4% faster than groups of up to 16 and than 8, A/B on one
+// box; 16 had measured 0.5-1% faster than 8 with a fully static order)
 #ifndef MOE_TILE_GM_GU
 #define MOE_TILE_GM_GU 8
+#endif
+#ifndef MOE_TILE_GM_GU_LONG
+#define MOE_TILE_GM_GU_LONG 12
 #endif
 // bf16 activations use the direct-to-LDS kernel below (1) or the register-staged one (0)
 #ifndef MOE_TILE_DMA
@@ -391,7 +396,7 @@ void ffn_tiled_dma_kernel(
   // given), else the static order throughout (claimed_tail_tile, static_tile)
   __shared__ int s_tile;
   int e, row0, nrows, nt;
-  constexpr int GM_LONG = kGateUp ? 2 * GM : GM;
+  constexpr int GM_LONG = kGateUp ? MOE_TILE_GM_GU_LONG : GM;
   {
     const TileGrid g = tile_grid<BM>(offsets, E, n_tiles_n, kXcds, claims ? 1 : xcd_grain(kGateUp, n_tiles_n));
     int tile;

@@ -144,6 +144,29 @@ def test_permute_bit_exact(T, K, E, kind):
     assert np.array_equal(s2r.cpu().numpy(), rr)
 
 
+@pytest.mark.parametrize("T,K,E", [(6000, 2, 16), (9000, 3, 64)])
+def test_permute_many_slots_out_of_range_ids_are_not_placed(T, K, E):
+    """The multi-workgroup permutation (many slots) with ids outside [0, E): the
+    valid slots keep the order of a stable sort, invalid ones map to -1, and the
+    sorted rows past the valid ones hold -1."""
+    rng = np.random.default_rng(T)
+    ids = rng.integers(0, E, size=(T, K)).astype(np.int32)
+    bad = rng.random((T, K)) < 0.01
+    ids[bad] = np.where(rng.random(int(bad.sum())) < 0.5, -1, E)
+    off, ss, s2r = moe_permute(torch.from_numpy(ids).cuda(), E)
+    torch.cuda.synchronize()
+    flat = ids.reshape(-1)
+    valid = (flat >= 0) & (flat < E)
+    n = int(valid.sum())
+    order = np.nonzero(valid)[0][np.argsort(flat[valid], kind="stable")]
+    ro, rs, rr = omoe.permute(flat[valid].reshape(-1, 1), E)
+    assert np.array_equal(off.cpu().numpy(), ro)
+    ss_h, s2r_h = ss.cpu().numpy(), s2r.cpu().numpy()
+    assert np.array_equal(ss_h[:n], order) and np.all(ss_h[n:] == -1)
+    assert np.all(s2r_h[~valid] == -1)
+    assert np.array_equal(s2r_h[order], np.arange(n))
+
+
 def test_permute_out_of_range_ids_are_not_placed():
     ids = np.array([[0, 3], [16, 1], [2, -1]], dtype=np.int32)
     off, ss, s2r = moe_permute(torch.from_numpy(ids).cuda(), 16)
