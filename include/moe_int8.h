@@ -286,6 +286,19 @@ moe_status moe_quantize_rows(int64_t rows, int32_t cols, int32_t src_dtype, cons
 moe_status moe_quantize_rows_fp8(int64_t rows, int32_t cols, int32_t src_dtype, const void* w,
                                  int32_t scale_dtype, uint8_t* q, void* s, hipStream_t stream);
 
+/* Quantizer and packer in one pass (load time: "Serving Considerations and
+ * Improvements", quantized in seconds when the model is loaded): the codes of
+ * moe_quantize_rows (weight_fmt MOE_W_INT8) or moe_quantize_rows_fp8
+ * (MOE_W_FP8), written straight into the tiled layout of moe_pack_rows, so
+ * the weights are read and the codes written once. Same scales, same codes
+ * bit for bit as quantizing then packing.
+ *   w [rows, cols] src_dtype in (rows % 16 == 0, cols % 64 == 0),
+ *   q_tiled [rows*cols] bytes out (tiled layout), s [rows] scale_dtype out.
+ * Errors as moe_quantize_rows; other weight_fmt values: MOE_ERR_DTYPE. */
+moe_status moe_quantize_pack_rows(int64_t rows, int32_t cols, int32_t src_dtype, const void* w,
+                                  int32_t scale_dtype, int32_t weight_fmt, void* q_tiled, void* s,
+                                  hipStream_t stream);
+
 /* Tiled int8 layout of the expert weights (load time, next to the quantizer).
  * The kernels read a wavefront's MFMA operands as whole 1 KiB blocks: a
  * row-major int8 matrix q [rows, cols] (rows % 16 == 0, cols % 64 == 0) is

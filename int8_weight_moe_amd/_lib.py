@@ -26,7 +26,7 @@ EXPORTS = (
     "moe_abi_version", "moe_status_str", "moe_last_error", "moe_workspace_size", "moe_ffn_workspace_size",
     "moe_route", "moe_permute", "moe_expert_ffn", "moe_expert_gate_up", "moe_expert_down", "moe_combine", "moe_forward", "moe_quantize_rows",
     "moe_pack_rows", "moe_mlp_workspace_size", "moe_mlp_forward", "moe_quantize_rows_fp8", "moe_down_workspace_size",
-    "moe_forward_noalloc", "moe_gate_up_workspace_size",
+    "moe_forward_noalloc", "moe_gate_up_workspace_size", "moe_quantize_pack_rows",
 )
 
 
@@ -62,6 +62,8 @@ _SIGS = {
     "moe_quantize_rows": (ctypes.c_int32, [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_int32, _P, _P, _P]),
     "moe_quantize_rows_fp8": (ctypes.c_int32, [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_int32, _P, _P, _P]),
     "moe_pack_rows": (ctypes.c_int32, [ctypes.c_int64, ctypes.c_int32, _P, _P, _P]),
+    "moe_quantize_pack_rows": (ctypes.c_int32, [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_int32,
+                                                ctypes.c_int32, _P, _P, _P]),
     "moe_mlp_workspace_size": (ctypes.c_int32, [_SHAPE, ctypes.POINTER(ctypes.c_size_t)]),
     "moe_mlp_forward": (ctypes.c_int32, [_SHAPE, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "moe_forward_noalloc": (ctypes.c_int32, [_SHAPE, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),

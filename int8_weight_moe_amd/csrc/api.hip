@@ -565,7 +565,7 @@ moe_status moe_quantize_rows(int64_t rows, int32_t cols, int32_t src_dtype, cons
   if (st != MOE_OK) return st;
   if (rows == 0) return MOE_OK;
   const hipError_t e = moe::launch_quantize_rows(rows, cols, src_dtype == MOE_BF16, w, scale_dtype == MOE_BF16, q,
-                                                 s, false, stream);
+                                                 s, false, false, stream);
   if (e != hipSuccess) return hip_fail(e, "quantize launch");
   return MOE_OK;
 }
@@ -576,7 +576,23 @@ moe_status moe_quantize_rows_fp8(int64_t rows, int32_t cols, int32_t src_dtype, 
   if (st != MOE_OK) return st;
   if (rows == 0) return MOE_OK;
   const hipError_t e = moe::launch_quantize_rows(rows, cols, src_dtype == MOE_BF16, w, scale_dtype == MOE_BF16,
-                                                 reinterpret_cast<int8_t*>(q), s, true, stream);
+                                                 reinterpret_cast<int8_t*>(q), s, true, false, stream);
+  if (e != hipSuccess) return hip_fail(e, "quantize launch");
+  return MOE_OK;
+}
+
+moe_status moe_quantize_pack_rows(int64_t rows, int32_t cols, int32_t src_dtype, const void* w,
+                                  int32_t scale_dtype, int32_t weight_fmt, void* q_tiled, void* s,
+                                  hipStream_t stream) {
+  moe_status st = check_quantize(rows, cols, src_dtype, w, scale_dtype, q_tiled, s);
+  if (st != MOE_OK) return st;
+  if (rows % 16 || cols % 64) return fail(MOE_ERR_SHAPE, "rows=%ld must be a multiple of 16 and cols=%d of 64", (long)rows, cols);
+  if (weight_fmt != MOE_W_INT8 && weight_fmt != MOE_W_FP8)
+    return fail(MOE_ERR_DTYPE, "weight_fmt=%d: only the int8 and fp8 encodings are quantized", weight_fmt);
+  if (rows == 0) return MOE_OK;
+  const hipError_t e = moe::launch_quantize_rows(rows, cols, src_dtype == MOE_BF16, w, scale_dtype == MOE_BF16,
+                                                 static_cast<int8_t*>(q_tiled), s, weight_fmt == MOE_W_FP8, true,
+                                                 stream);
   if (e != hipSuccess) return hip_fail(e, "quantize launch");
   return MOE_OK;
 }

@@ -19,9 +19,10 @@
 // result is the canonical +0 byte. The e4m3 midpoints have at most 5
 // significant bits, so the same exactness argument holds.
 //
-// One workgroup per row: pass 1 reduces max|w| (16-byte loads, wave shuffles,
-// then LDS across waves), pass 2 re-reads the row (mostly from L2) and writes
-// 16 codes per 16-byte store.
+// Row-major codes: one workgroup per row: pass 1 reduces max|w| (16-byte
+// loads, wave shuffles, then LDS across waves), pass 2 re-reads the row
+// (mostly from L2) and writes 16 codes per 16-byte store. Codes in the tiled
+// layout of the expert kernels: one workgroup per 16 rows (below).
 #include "device_common.h"
 #include "kernels.h"
 
@@ -91,7 +92,19 @@ __device__ __forceinline__ void load16(const void* w, long idx, float (&v)[16]) 
   }
 }
 
-template <bool kSrcBf16, bool kScaleBf16, bool kFp8>
+// Byte offset of the 16 codes of row `row`, columns c .. c+15 (c % 16 == 0):
+// row-major, or the tiled layout (block (row/16, c/64) at block index
+// (row/16)*(cols/64) + c/64, piece 16*(row%16) + 256*((c%64)/16) inside it).
+template <bool kTiled>
+__device__ __forceinline__ long code_offset(long row, int c, int cols) {
+  if constexpr (kTiled) {
+    return ((row >> 4) * (cols >> 6) + (c >> 6)) * 1024 + 256 * ((c & 63) >> 4) + 16 * (row & 15);
+  } else {
+    return row * cols + c;
+  }
+}
+
+template <bool kSrcBf16, bool kScaleBf16, bool kFp8, bool kTiled>
 __global__ __launch_bounds__(kQuantThreads) void quantize_rows_kernel(const void* __restrict__ w, int cols,
                                                                       int8_t* __restrict__ q, void* __restrict__ s) {
   __shared__ float wmax[kQuantThreads / kWave];
@@ -148,27 +161,112 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_rows_kernel(const void
         packed[i >> 2] |= b << (8 * (i & 3));
       }
     }
-    *reinterpret_cast<uint4*>(q + base + c) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+    *reinterpret_cast<uint4*>(q + code_offset<kTiled>(row, c, cols)) =
+        make_uint4(packed[0], packed[1], packed[2], packed[3]);
   }
 }
 
-template <bool kFp8>
+// Tiled output: one workgroup per 16-row group (the rows of one row of
+// blocks). Pass 1: wave w reduces max|w| of rows 4w .. 4w+3 and the 16 scales
+// go through LDS. Pass 2: every store of a wave writes one whole 1 KiB block
+// (lane l: row l%16, columns 16*(l/16) .. +16 of the block), read back from L2.
+template <bool kSrcBf16, bool kScaleBf16, bool kFp8>
+__global__ __launch_bounds__(kQuantThreads) void quantize_pack_kernel(const void* __restrict__ w, int cols,
+                                                                      int8_t* __restrict__ q, void* __restrict__ s) {
+  constexpr int kRowsPerWave = 16 / (kQuantThreads / kWave);
+  __shared__ double scale_of[16];
+  const long rg = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int i = 0; i < kRowsPerWave; ++i) {
+    const long row = rg * 16 + wave * kRowsPerWave + i;
+    float m = 0.f;
+    for (int c = lane * 16; c < cols; c += kWave * 16) {
+      float v[16];
+      load16<kSrcBf16>(w, row * cols + c, v);
+#pragma unroll
+      for (int k = 0; k < 16; ++k) m = fmaxf(m, fabsf(v[k]));
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+    const double sd = (double)m / (kFp8 ? 448.0 : 127.0);
+    double scale;
+    if constexpr (kScaleBf16) {
+      scale = round_f64_to_bf16(sd);
+    } else {
+      scale = (double)(float)sd;  // IEEE conversion: round to nearest even
+    }
+    if (lane == 0) {
+      scale_of[wave * kRowsPerWave + i] = scale;
+      if constexpr (kScaleBf16) {
+        static_cast<uint16_t*>(s)[row] = (uint16_t)(__float_as_uint((float)scale) >> 16);
+      } else {
+        static_cast<float*>(s)[row] = (float)scale;
+      }
+    }
+  }
+  __syncthreads();
+  const int r = lane & 15;
+  const long row = rg * 16 + r;
+  const double scale = scale_of[r];
+  const int kblocks = cols >> 6;
+  for (int ks = wave; ks < kblocks; ks += kQuantThreads / kWave) {
+    const int c = ks * 64 + 16 * (lane >> 4);
+    float v[16];
+    load16<kSrcBf16>(w, row * cols + c, v);
+    uint32_t packed[4] = {0u, 0u, 0u, 0u};
+    if (scale > 0.0) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        uint32_t b;
+        if constexpr (kFp8) {
+          b = encode_e4m3((double)v[i] / scale);
+        } else {
+          double rr = rint((double)v[i] / scale);
+          rr = fmin(fmax(rr, -127.0), 127.0);
+          b = (uint32_t)(uint8_t)(int8_t)(int)rr;
+        }
+        packed[i >> 2] |= b << (8 * (i & 3));
+      }
+    }
+    *reinterpret_cast<uint4*>(q + code_offset<true>(row, c, cols)) =
+        make_uint4(packed[0], packed[1], packed[2], packed[3]);
+  }
+}
+
+template <bool kFp8, bool kTiled>
 hipError_t launch_quantize(int64_t rows, int cols, bool src_bf16, const void* w, bool scale_bf16, int8_t* q, void* s,
                            hipStream_t stream) {
   if (rows == 0) return hipSuccess;
   const dim3 block(kQuantThreads);
+  if constexpr (kTiled) {
+    const dim3 grid((unsigned)(rows / 16));
+    if (src_bf16) {
+      if (scale_bf16)
+        hipLaunchKernelGGL((quantize_pack_kernel<true, true, kFp8>), grid, block, 0, stream, w, cols, q, s);
+      else
+        hipLaunchKernelGGL((quantize_pack_kernel<true, false, kFp8>), grid, block, 0, stream, w, cols, q, s);
+    } else {
+      if (scale_bf16)
+        hipLaunchKernelGGL((quantize_pack_kernel<false, true, kFp8>), grid, block, 0, stream, w, cols, q, s);
+      else
+        hipLaunchKernelGGL((quantize_pack_kernel<false, false, kFp8>), grid, block, 0, stream, w, cols, q, s);
+    }
+    return hipGetLastError();
+  }
   // grid.x is limited to 2^31-1; rows beyond that are rejected by the caller
   const dim3 grid((unsigned)rows);
   if (src_bf16) {
     if (scale_bf16)
-      hipLaunchKernelGGL((quantize_rows_kernel<true, true, kFp8>), grid, block, 0, stream, w, cols, q, s);
+      hipLaunchKernelGGL((quantize_rows_kernel<true, true, kFp8, false>), grid, block, 0, stream, w, cols, q, s);
     else
-      hipLaunchKernelGGL((quantize_rows_kernel<true, false, kFp8>), grid, block, 0, stream, w, cols, q, s);
+      hipLaunchKernelGGL((quantize_rows_kernel<true, false, kFp8, false>), grid, block, 0, stream, w, cols, q, s);
   } else {
     if (scale_bf16)
-      hipLaunchKernelGGL((quantize_rows_kernel<false, true, kFp8>), grid, block, 0, stream, w, cols, q, s);
+      hipLaunchKernelGGL((quantize_rows_kernel<false, true, kFp8, false>), grid, block, 0, stream, w, cols, q, s);
     else
-      hipLaunchKernelGGL((quantize_rows_kernel<false, false, kFp8>), grid, block, 0, stream, w, cols, q, s);
+      hipLaunchKernelGGL((quantize_rows_kernel<false, false, kFp8, false>), grid, block, 0, stream, w, cols, q, s);
   }
   return hipGetLastError();
 }
@@ -176,9 +274,13 @@ hipError_t launch_quantize(int64_t rows, int cols, bool src_bf16, const void* w,
 }  // namespace
 
 hipError_t launch_quantize_rows(int64_t rows, int cols, bool src_bf16, const void* w, bool scale_bf16, int8_t* q,
-                                void* s, bool fp8, hipStream_t stream) {
-  return fp8 ? launch_quantize<true>(rows, cols, src_bf16, w, scale_bf16, q, s, stream)
-             : launch_quantize<false>(rows, cols, src_bf16, w, scale_bf16, q, s, stream);
+                                void* s, bool fp8, bool tiled, hipStream_t stream) {
+  if (tiled) {
+    return fp8 ? launch_quantize<true, true>(rows, cols, src_bf16, w, scale_bf16, q, s, stream)
+               : launch_quantize<false, true>(rows, cols, src_bf16, w, scale_bf16, q, s, stream);
+  }
+  return fp8 ? launch_quantize<true, false>(rows, cols, src_bf16, w, scale_bf16, q, s, stream)
+             : launch_quantize<false, false>(rows, cols, src_bf16, w, scale_bf16, q, s, stream);
 }
 
 }  // namespace moe

@@ -335,6 +335,19 @@ def moe_quantize_rows_fp8(w: torch.Tensor, scale_dtype: torch.dtype):
     return q, s
 
 
+def moe_quantize_pack_rows(w: torch.Tensor, scale_dtype: torch.dtype, fmt: int = MOE_W_INT8):
+    """Quantize w [..., rows, cols] (int8 or fp8 e4m3 codes) straight into the tiled layout:
+    (codes [..., rows, cols] in the tiled byte order, scales [..., rows]), one pass."""
+    lib = _lib_handle()
+    cols = w.shape[-1]
+    rows = w.numel() // cols
+    q = torch.empty(w.shape, dtype=torch.int8 if fmt == MOE_W_INT8 else torch.uint8, device=w.device)
+    s = torch.empty(w.shape[:-1], dtype=scale_dtype, device=w.device)
+    _lib.check(lib.moe_quantize_pack_rows(ctypes.c_int64(rows), ctypes.c_int32(cols), _dtype_code(w.dtype), _ptr(w),
+                                          _dtype_code(scale_dtype), ctypes.c_int32(fmt), _ptr(q), _ptr(s), _stream()))
+    return q, s
+
+
 def moe_pack_rows(q: torch.Tensor) -> torch.Tensor:
     """Row-major int8 codes [..., rows, cols] -> the tiled layout (same shape, permuted bytes)."""
     lib = _lib_handle()
@@ -364,24 +377,22 @@ def pack_experts(q_gate: torch.Tensor, q_up: torch.Tensor, q_down: torch.Tensor,
 
 def quantize_experts_fp8(w_gate: torch.Tensor, w_up: torch.Tensor, w_down: torch.Tensor,
                          scale_dtype: torch.dtype) -> Int8Experts:
-    """FP8 comparator: quantize the (out, in) expert weights to e4m3 codes, then tile the bytes."""
+    """FP8 comparator: quantize the (out, in) expert weights to e4m3 codes in the tiled layout (one pass)."""
     out, scales = [], []
     for w in (w_gate, w_up, w_down):
-        q, s = moe_quantize_rows_fp8(w, scale_dtype)
-        out.append(moe_pack_rows(q.view(torch.int8)).view(torch.uint8))
+        q, s = moe_quantize_pack_rows(w, scale_dtype, MOE_W_FP8)
+        out.append(q)
         scales.append(s)
-        del q
     return Int8Experts(out[0], out[1], out[2], scales[0], scales[1], scales[2], fmt=MOE_W_FP8)
 
 
 def quantize_experts(w_gate: torch.Tensor, w_up: torch.Tensor, w_down: torch.Tensor,
                      scale_dtype: torch.dtype) -> Int8Experts:
-    """Load-time ExpertsInt8: quantize the (out, in) expert weights, then tile the codes."""
+    """Load-time ExpertsInt8: quantize the (out, in) expert weights straight into the tiled layout (one pass)."""
     out = []
     scales = []
     for w in (w_gate, w_up, w_down):
-        q, s = moe_quantize_rows(w, scale_dtype)
-        out.append(moe_pack_rows(q))
+        q, s = moe_quantize_pack_rows(w, scale_dtype, MOE_W_INT8)
+        out.append(q)
         scales.append(s)
-        del q
     return Int8Experts(out[0], out[1], out[2], scales[0], scales[1], scales[2])

@@ -108,6 +108,11 @@ int main(void) {
   CHECK(moe_quantize_rows(16, 64, MOE_BF16, A, MOE_BF16, A, (char*)A + 2, NULL) == MOE_ERR_ALIGN);
   CHECK(moe_quantize_rows_fp8(16, 64, MOE_BF16, A, MOE_BF16, NULL, A, NULL) == MOE_ERR_NULL);
   CHECK(moe_quantize_rows(0, 64, MOE_BF16, A, MOE_BF16, A, A, NULL) == MOE_OK);
+  CHECK(moe_quantize_pack_rows(24, 64, MOE_BF16, A, MOE_BF16, MOE_W_INT8, A, A, NULL) == MOE_ERR_SHAPE);
+  CHECK(moe_quantize_pack_rows(32, 80, MOE_BF16, A, MOE_BF16, MOE_W_INT8, A, A, NULL) == MOE_ERR_SHAPE);
+  CHECK(moe_quantize_pack_rows(32, 64, MOE_BF16, A, MOE_BF16, MOE_W_BF16, A, A, NULL) == MOE_ERR_DTYPE);
+  CHECK(moe_quantize_pack_rows(32, 64, MOE_BF16, A, MOE_BF16, MOE_W_FP8, NULL, A, NULL) == MOE_ERR_NULL);
+  CHECK(moe_quantize_pack_rows(0, 64, MOE_BF16, A, MOE_BF16, MOE_W_FP8, A, A, NULL) == MOE_OK);
   CHECK(moe_pack_rows(17, 64, A, A, NULL) == MOE_ERR_SHAPE);
   CHECK(moe_pack_rows(16, 96, A, A, NULL) == MOE_ERR_SHAPE);
   CHECK(moe_pack_rows(16, 64, A, A, NULL) == MOE_ERR_UNSUPPORTED);   /* in place */

@@ -10,8 +10,9 @@ import torch
 
 import workloads
 from int8_weight_moe_amd import (MoeError, moe_combine, moe_expert_down, moe_expert_ffn, moe_expert_gate_up, moe_forward,
-                                 moe_mlp_forward, moe_pack_rows, moe_permute, moe_quantize_rows, moe_route)
-from int8_weight_moe_amd._lib import MOE_PATH_AUTO, MOE_PATH_STREAM, MOE_PATH_TILED
+                                 moe_mlp_forward, moe_pack_rows, moe_permute, moe_quantize_pack_rows, moe_quantize_rows,
+                                 moe_quantize_rows_fp8, moe_route)
+from int8_weight_moe_amd._lib import MOE_PATH_AUTO, MOE_PATH_STREAM, MOE_PATH_TILED, MOE_W_FP8, MOE_W_INT8
 from oracle import moe as omoe
 from oracle import quant as oquant
 from tests.helpers import (assert_close_to_oracle, check_routing, experts_to_device, np64,
@@ -48,6 +49,31 @@ def test_quantize_rows_bit_exact(src, scale):
     qr, sr = oquant.quantize_rows(np64(wt), scale)
     assert np.array_equal(q.cpu().numpy(), qr)
     assert np.array_equal(np64(s), sr)
+
+
+@pytest.mark.parametrize("fmt", [MOE_W_INT8, MOE_W_FP8])
+@pytest.mark.parametrize("src,scale,rows,cols", [("bf16", "bf16", 48, 320), ("f32", "f32", 16, 64),
+                                                 ("bf16", "bf16", 3 * 512, 4096), ("f32", "bf16", 64, 192)])
+def test_quantize_pack_rows_equals_quantize_then_pack(fmt, src, scale, rows, cols):
+    """The one-pass quantizer writes the codes of the row-major quantizer straight
+    into the tiled layout: equal to quantize-then-pack bit for bit, same scales;
+    the int8 codes, untiled, equal the oracle's."""
+    rng = np.random.default_rng(rows + cols)
+    w = rng.standard_normal((rows, cols)).astype(np.float32) * np.float32(0.02)
+    w[5] = 0.0                                          # a zero row
+    wt = torch.from_numpy(w).to(TDT[src]).cuda()
+    qt, st = moe_quantize_pack_rows(wt, TDT[scale], fmt)
+    if fmt == MOE_W_INT8:
+        q, s = moe_quantize_rows(wt, TDT[scale])
+    else:
+        q, s = moe_quantize_rows_fp8(wt, TDT[scale])
+    p = moe_pack_rows(q.view(torch.int8))
+    torch.cuda.synchronize()
+    assert torch.equal(qt.view(torch.int8), p) and torch.equal(st, s)
+    if fmt == MOE_W_INT8:
+        qr, sr = oquant.quantize_rows(np64(wt), scale)
+        assert np.array_equal(tiled_to_rowmajor(qt.cpu().numpy()), qr)
+        assert np.array_equal(np64(st), sr)
 
 
 @pytest.mark.parametrize("rows,cols", [(16, 64), (48, 320), (3 * 512, 256), (16 * 64, 4096)])
