@@ -42,6 +42,22 @@
  *   - Slots: token t's k-th choice is slot s = t*K + k.
  *   - T = 0 is valid and enqueues nothing; once the shape is valid, no
  *     pointer is then checked (empty tensors may be NULL).
+ *   - Debug checks: while the environment variable MOE_DEBUG is set (to a
+ *     value other than "0"), the calls that take or produce a permutation
+ *     also check it, on the host:
+ *       moe_expert_ffn, moe_expert_gate_up, moe_expert_down: expert_offsets
+ *         starts at 0, never decreases and ends at most at T*K; for the first
+ *         two, the sorted rows below off[E] hold distinct slots in [0, T*K);
+ *       moe_combine: every slot_to_row entry is -1 or in [0, T*K);
+ *       these run BEFORE anything is launched, so bad caller arrays are
+ *       reported instead of being read out of bounds by a kernel;
+ *       moe_permute, moe_forward, moe_forward_noalloc: after the permutation
+ *         is computed, also that every id is in [0, E) (all slots placed),
+ *         that each expert's rows hold its own slots in ascending order and
+ *         that slot_to_row inverts sorted_slots.
+ *     A failed check returns MOE_ERR_CHECK (moe_forward: before the down
+ *     pass). The checks copy the arrays to the host and synchronise `stream`:
+ *     they are for debugging, not for timed runs or graph capture.
  */
 #ifndef MOE_INT8_H
 #define MOE_INT8_H
@@ -63,7 +79,8 @@ enum {
   MOE_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned */
   MOE_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required */
   MOE_ERR_UNSUPPORTED = 6, /* valid request the library does not support */
-  MOE_ERR_HIP = 7          /* a HIP runtime call failed */
+  MOE_ERR_HIP = 7,         /* a HIP runtime call failed */
+  MOE_ERR_CHECK = 8        /* a MOE_DEBUG consistency check failed */
 };
 
 /* dtype codes */
@@ -103,7 +120,7 @@ typedef struct moe_shape {
 } moe_shape;
 
 /* ABI version of this header (bumped on any signature change). */
-#define MOE_ABI_VERSION 5
+#define MOE_ABI_VERSION 6
 int32_t moe_abi_version(void);
 
 /* Static description of a status code. */

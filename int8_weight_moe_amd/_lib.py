@@ -11,11 +11,12 @@ import os
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libmoe_int8.so")
 
-ABI_VERSION = 5
+ABI_VERSION = 6
 MOE_OK = 0
 STATUS_NAMES = {
     0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_DTYPE", 4: "MOE_ERR_ALIGN",
     5: "MOE_ERR_WORKSPACE", 6: "MOE_ERR_UNSUPPORTED", 7: "MOE_ERR_HIP",
+    8: "MOE_ERR_CHECK",
 }
 MOE_F32, MOE_BF16 = 0, 1
 MOE_PATH_AUTO, MOE_PATH_STREAM, MOE_PATH_TILED = 0, 1, 2

@@ -1,13 +1,18 @@
 // C ABI of libmoe_int8: argument validation, workspace layout and the
-// enqueueing of the kernels. Nothing here allocates memory or synchronises.
+// enqueueing of the kernels. Nothing here allocates device memory or
+// synchronises, except the checks that MOE_DEBUG turns on.
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <atomic>
 #include <mutex>
+#include <string>
+#include <vector>
 
 #include "../../include/moe_int8.h"
+#include "debug_checks.h"
 #include "kernels.h"
 
 namespace {
@@ -28,6 +33,63 @@ moe_status hip_fail(hipError_t e, const char* what) {
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// ---- MOE_DEBUG: permutation checks on the host (debug runs only)
+
+// Set and not "0" at the time of the call.
+bool debug_on() {
+  const char* v = getenv("MOE_DEBUG");
+  return v && v[0] && strcmp(v, "0") != 0;
+}
+
+// n int32 values from the device, after the work already enqueued on `stream`.
+moe_status fetch_ints(const int32_t* dev, long n, std::vector<int32_t>& out, hipStream_t stream) {
+  out.assign((size_t)n, 0);
+  if (n <= 0) return MOE_OK;
+  hipError_t e = hipMemcpyAsync(out.data(), dev, (size_t)n * sizeof(int32_t), hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "MOE_DEBUG copy to the host");
+}
+
+moe_status debug_verdict(const std::string& m, const char* what) {
+  return m.empty() ? MOE_OK : fail(MOE_ERR_CHECK, "MOE_DEBUG %s: %s", what, m.c_str());
+}
+
+// A caller's segment offsets and, when `sorted` is given, the slots of the
+// rows they cover.
+moe_status debug_inputs(const moe_shape* s, const int32_t* offsets, const int32_t* sorted, hipStream_t stream) {
+  const long S = (long)s->T * s->K;
+  std::vector<int32_t> off, srt;
+  moe_status st = fetch_ints(offsets, s->E + 1, off, stream);
+  if (st != MOE_OK) return st;
+  st = debug_verdict(moe_debug::check_offsets(off.data(), s->E, S), "expert_offsets");
+  if (st != MOE_OK || !sorted) return st;
+  if ((st = fetch_ints(sorted, off[s->E], srt, stream)) != MOE_OK) return st;
+  return debug_verdict(moe_debug::check_sorted(srt.data(), off[s->E], S), "sorted_slots");
+}
+
+// A caller's slot_to_row.
+moe_status debug_rows(const moe_shape* s, const int32_t* s2r, hipStream_t stream) {
+  const long S = (long)s->T * s->K;
+  std::vector<int32_t> rows;
+  moe_status st = fetch_ints(s2r, S, rows, stream);
+  if (st != MOE_OK) return st;
+  return debug_verdict(moe_debug::check_rows(rows.data(), S), "slot_to_row");
+}
+
+// The permutation the library produced from the expert ids.
+moe_status debug_permutation(const moe_shape* s, const int32_t* ids, const int32_t* offsets, const int32_t* sorted,
+                             const int32_t* s2r, hipStream_t stream) {
+  const long S = (long)s->T * s->K;
+  std::vector<int32_t> i, off, srt, rows;
+  moe_status st;
+  if ((st = fetch_ints(ids, S, i, stream)) != MOE_OK) return st;
+  if ((st = fetch_ints(offsets, s->E + 1, off, stream)) != MOE_OK) return st;
+  if ((st = fetch_ints(sorted, S, srt, stream)) != MOE_OK) return st;
+  if ((st = fetch_ints(s2r, S, rows, stream)) != MOE_OK) return st;
+  return debug_verdict(moe_debug::check_permutation(i.data(), off.data(), srt.data(), rows.data(), s->E, S),
+                       "permutation");
+}
 
 constexpr size_t kAlign = 256;
 size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
@@ -269,9 +331,14 @@ moe_status forward_impl(const moe_shape* s, const void* x, const void* router_w,
     a.perm_s2r = s2r;
     st = run_gate_up(s, a, stream);
     a.ids = nullptr;
+    if (st == MOE_OK && debug_on()) st = debug_permutation(s, ids, offsets, sorted, s2r, stream);
   } else {
     e = moe::launch_permute(ids, s->T * s->K, s->E, offsets, sorted, s2r, stream);
     if (e != hipSuccess) return hip_fail(e, "permute launch");
+    if (debug_on()) {
+      st = debug_permutation(s, ids, offsets, sorted, s2r, stream);
+      if (st != MOE_OK) return st;
+    }
     st = run_gate_up(s, a, stream);
   }
   if (st != MOE_OK) return st;
@@ -298,6 +365,7 @@ const char* moe_status_str(moe_status st) {
     case MOE_ERR_WORKSPACE: return "workspace too small";
     case MOE_ERR_UNSUPPORTED: return "unsupported request";
     case MOE_ERR_HIP: return "HIP runtime error";
+    case MOE_ERR_CHECK: return "MOE_DEBUG check failed";
     default: return "unknown status";
   }
 }
@@ -348,6 +416,7 @@ moe_status moe_permute(const moe_shape* s, const int32_t* topk_ids, int32_t* exp
   const hipError_t e = moe::launch_permute(topk_ids, s->T * s->K, s->E, expert_offsets, sorted_slots,
                                            slot_to_row, stream);
   if (e != hipSuccess) return hip_fail(e, "permute launch");
+  if (debug_on()) return debug_permutation(s, topk_ids, expert_offsets, sorted_slots, slot_to_row, stream);
   return MOE_OK;
 }
 
@@ -374,6 +443,7 @@ moe_status moe_expert_ffn(const moe_shape* s, const void* x, const int32_t* expe
   const size_t need = ffn_ws_bytes(s);
   if (workspace_bytes < need)
     return fail(MOE_ERR_WORKSPACE, "workspace_bytes=%zu < required %zu", workspace_bytes, need);
+  if (debug_on() && (st = debug_inputs(s, expert_offsets, sorted_slots, stream)) != MOE_OK) return st;
   moe::FfnArgs a = ffn_args(s, x, expert_offsets, sorted_slots, w_gate, w_up, w_down, s_gate, s_up, s_down, y_rows,
                             static_cast<__bf16*>(workspace));
   char* dws = static_cast<char*>(workspace) + ffn_h_bytes(s);
@@ -411,6 +481,7 @@ moe_status moe_expert_gate_up(const moe_shape* s, const void* x, const int32_t* 
     if (workspace_bytes < need)
       return fail(MOE_ERR_WORKSPACE, "workspace_bytes=%zu < required %zu", workspace_bytes, need);
   }
+  if (debug_on() && (st = debug_inputs(s, expert_offsets, sorted_slots, stream)) != MOE_OK) return st;
   moe::FfnArgs a = ffn_args(s, x, expert_offsets, sorted_slots, w_gate, w_up, nullptr, s_gate, s_up, nullptr,
                             nullptr, static_cast<__bf16*>(h));
   if (workspace && need) a.claims_gate_up = static_cast<unsigned long long*>(workspace);
@@ -436,6 +507,7 @@ moe_status moe_expert_down(const moe_shape* s, const void* h, const int32_t* exp
     if (workspace_bytes < need)
       return fail(MOE_ERR_WORKSPACE, "workspace_bytes=%zu < required %zu", workspace_bytes, need);
   }
+  if (debug_on() && (st = debug_inputs(s, expert_offsets, nullptr, stream)) != MOE_OK) return st;
   moe::FfnArgs a = ffn_args(s, nullptr, expert_offsets, nullptr, nullptr, nullptr, w_down, nullptr, nullptr, s_down,
                             y_rows, static_cast<__bf16*>(const_cast<void*>(h)));
   if (workspace && need) {
@@ -473,6 +545,7 @@ moe_status moe_combine(const moe_shape* s, const float* y_rows, const int32_t* s
   REQUIRE_PTR(slot_to_row);
   REQUIRE_PTR(topk_w);
   REQUIRE_PTR(y);
+  if (debug_on() && (st = debug_rows(s, slot_to_row, stream)) != MOE_OK) return st;
   const hipError_t e = moe::launch_combine(y_rows, slot_to_row, topk_w, s->T, s->d, s->K,
                                            s->act_dtype == MOE_BF16, y, stream);
   if (e != hipSuccess) return hip_fail(e, "combine launch");
