@@ -130,18 +130,31 @@ def time_forward(layer, x, path, steps, warmup, dense=False):
     One timed region of `steps` back-to-back calls bracketed by synchronisations;
     a HIP event after every call also gives each step's own duration. Returns
     (ms per step over the region, wall ms per step, [per-step ms])."""
+    import ctypes
     import torch
-    from int8_weight_moe_amd import moe_mlp_forward
+    from int8_weight_moe_amd import _lib
+    from int8_weight_moe_amd.ops import _ptr, _stream
     y = torch.empty_like(x)
     ids = torch.empty((x.shape[0], layer.K), dtype=torch.int32, device=x.device)
     gw = torch.empty((x.shape[0], layer.K), dtype=torch.float32, device=x.device)
-    ws = layer.workspace(layer.shape(x, path))
+    shape = layer.shape(x, path)
+    ws = layer.workspace(shape)
+    ex = layer.experts
+    # the C call with its arguments marshalled once: at decode sizes the
+    # per-call Python marshalling would otherwise approach the step's GPU time
+    lib = _lib.load()
+    weights = (_ptr(ex.q_gate), _ptr(ex.q_up), _ptr(ex.q_down), _ptr(ex.s_gate), _ptr(ex.s_up), _ptr(ex.s_down))
+    tail = (_ptr(ws), ctypes.c_size_t(ws.numel()), _stream())
+    if dense:
+        fn, args = lib.moe_mlp_forward, (ctypes.byref(shape), _ptr(x), *weights, _ptr(y), *tail)
+    else:
+        fn, args = lib.moe_forward, (ctypes.byref(shape), _ptr(x), _ptr(layer.router_w), _ptr(layer.bias), *weights,
+                                     _ptr(y), _ptr(ids), _ptr(gw), *tail)
 
     def step():
-        if dense:
-            moe_mlp_forward(x, layer.experts, path=path, y=y, workspace=ws)
-        else:
-            layer.forward(x, path=path, y=y, ids=ids, w=gw)
+        st = fn(*args)
+        if st:
+            _lib.check(st)
 
     for _ in range(warmup):
         step()
@@ -168,6 +181,26 @@ def spread(per_step):
         hi = min(lo + 1, len(v) - 1)
         return v[lo] + (v[hi] - v[lo]) * (k - lo)
     return {"p10_ms": round(q(0.1), 4), "p50_ms": round(q(0.5), 4), "p90_ms": round(q(0.9), 4)}
+
+
+# host time per staged call (ms), generous: the wrappers allocate nothing but
+# build a shape and query a workspace size per call
+_STAGE_HOST_MS = {"route": 0.1, "permute": 0.1, "gate_up": 0.1, "down": 0.1, "combine": 0.1}
+_SPIN_MS_PER_MCYCLE = []
+
+
+def gpu_lead(ms):
+    """Enqueue a spin kernel that keeps the GPU busy for about `ms` (at most 100)."""
+    import torch
+    if not _SPIN_MS_PER_MCYCLE:
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        torch.cuda._sleep(1_000_000)
+        e1.record()
+        e1.synchronize()
+        _SPIN_MS_PER_MCYCLE.append(max(e0.elapsed_time(e1), 1e-3))
+    torch.cuda._sleep(int(min(ms, 100.0) / _SPIN_MS_PER_MCYCLE[0] * 1_000_000))
 
 
 def time_stages(layer, x, path, steps, warmup, dense=False):
@@ -215,6 +248,11 @@ def time_stages(layer, x, path, steps, warmup, dense=False):
     for _ in range(warmup):
         step([torch.cuda.Event(enable_timing=True) for _ in range(n_ev)])
     torch.cuda.synchronize()
+    # The staged calls cost more host time per step than a decode step takes on
+    # the GPU, so the GPU would idle between them and the idle time would count
+    # in the stage after it. A spin kernel ahead of the timed steps keeps the
+    # GPU busy while the host enqueues them; they then run back to back.
+    gpu_lead(1.5 * steps * sum(_STAGE_HOST_MS.get(n, 0.05) for n in names))
     for i in range(steps):
         step(evs[i])
     torch.cuda.synchronize()

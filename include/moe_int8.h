@@ -270,7 +270,10 @@ moe_status moe_forward_noalloc(const moe_shape* shape, const void* x, const void
  * layer is the MoE layer with one expert used by every token with weight 1:
  *   y = s_d * (q_d . h),  h = silu(s_g * (q_g . x)) * (s_u * (q_u . x)).
  * shape->E and shape->K must be 1; no router. Same kernels, weight encodings
- * and layouts as the MoE calls, same tolerance.
+ * and layouts as the MoE calls, same tolerance; the result is bitwise that of
+ * moe_expert_ffn followed by moe_combine with weight 1 (when the down pass
+ * splits its reduction over workgroups, the kernel that adds the slices
+ * writes y itself).
  *   y [T, d] act_dtype out; workspace >= moe_mlp_workspace_size bytes. */
 moe_status moe_mlp_workspace_size(const moe_shape* shape, size_t* bytes);
 moe_status moe_mlp_forward(const moe_shape* shape, const void* x,

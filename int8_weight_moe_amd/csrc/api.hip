@@ -208,6 +208,7 @@ moe::FfnArgs ffn_args(const moe_shape* s, const void* x, const int32_t* offsets,
   a.h = h;
   a.y_rows = y_rows;
   a.part = nullptr;
+  a.y_dense = nullptr;
   a.ids = nullptr;
   a.perm_offsets = a.perm_sorted = a.perm_s2r = nullptr;
   a.claims_gate_up = a.claims_down = nullptr;
@@ -623,10 +624,13 @@ moe_status moe_mlp_forward(const moe_shape* s, const void* x, const void* w_gate
     a.claims_gate_up = reinterpret_cast<unsigned long long*>(ws + L.claims);
     a.claims_down = reinterpret_cast<unsigned long long*>(ws + L.claims + moe::kTileClaimBytes);
   }
+  // with the down pass's reduction split over workgroups, the sum of its slices
+  // is written to y directly (the combine of one expert of weight 1)
+  if (L.part_bytes) a.y_dense = y;
   st = run_gate_up(s, a, stream);
   if (st != MOE_OK) return st;
   st = run_down(s, a, stream);
-  if (st != MOE_OK) return st;
+  if (st != MOE_OK || a.y_dense) return st;
   e = moe::launch_combine(y_rows, s2r, wts, s->T, s->d, 1, s->act_dtype == MOE_BF16, y, stream);
   if (e != hipSuccess) return hip_fail(e, "combine launch");
   return MOE_OK;

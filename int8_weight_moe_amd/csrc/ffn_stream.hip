@@ -116,8 +116,9 @@ namespace {
 #ifndef MOE_STREAM_P_SHARED
 #define MOE_STREAM_P_SHARED 6
 #endif
-// ring depth of that kernel's reduction-split shape (six waves: the registers
-// of two waves per SIMD leave room for four stages)
+// ring depth of that kernel's reduction-split shapes (six waves: the registers
+// of two waves per SIMD leave room for four stages; the one-wave-per-SIMD
+// shape measured the same with 3, 4 and 5 stages, slower with 6)
 #ifndef MOE_STREAM_P_SHARED_SPLIT
 #define MOE_STREAM_P_SHARED_SPLIT 4
 #endif
@@ -134,8 +135,17 @@ namespace {
 #ifndef MOE_STREAM_SHARED_DN_WAVES
 #define MOE_STREAM_SHARED_DN_WAVES 4
 #endif
+// 16-channel groups per wave of that kernel and its ring depth: one wave per
+// SIMD with 64-channel items streams the dense MLP's down pass best (A/B on
+// one box: 54.6 -> 50.3 us with an 8-deep ring, 51.0 with 6, 50.4 with 5;
+// 32-channel items with an 8-deep ring: 54.0). The reduction split is still
+// chosen from the 32-channel item count (MOE_STREAM_NG_DN_WIDE), so the
+// slices, and the result, are those of the in-workgroup split.
+#ifndef MOE_STREAM_NG_SHARED_DN
+#define MOE_STREAM_NG_SHARED_DN 4
+#endif
 #ifndef MOE_STREAM_P_SHARED_DN
-#define MOE_STREAM_P_SHARED_DN 6
+#define MOE_STREAM_P_SHARED_DN 8
 #endif
 constexpr int kStreamWaves = MOE_STREAM_WAVES;
 
@@ -785,11 +795,14 @@ __global__ __launch_bounds__(W * kWave) void ffn_stream_shared_dn_kernel(
 // scale of row r's expert (unscaled encodings: 1); rows of no expert are left
 // as they are. One workgroup per (row, 1024 channels), four channels a thread;
 // rows run along the grid's x axis (up to 2^26 of them), channel blocks along y.
-template <bool kScaleBf16, bool kScaled>
+// kOut 0: the sums go to y_rows (fp32). kOut 1 (bf16) or 2 (fp32): a dense
+// layer's output y, written as the combine writes a token with one expert of
+// weight 1 (0 + 1 * v, then the act dtype), so the result is the same bit for bit.
+template <bool kScaleBf16, bool kScaled, int kOut>
 __global__ __launch_bounds__(256) void split_down_reduce_kernel(const float* __restrict__ part, int KS, int S, int N,
                                                                 const int32_t* __restrict__ offsets, int E,
                                                                 const void* __restrict__ S0,
-                                                                float* __restrict__ y_rows) {
+                                                                void* __restrict__ out) {
   const int r = blockIdx.x;
   const int lane = threadIdx.x & 63;
   int o0 = 0, o1 = 0;
@@ -809,7 +822,21 @@ __global__ __launch_bounds__(256) void split_down_reduce_kernel(const float* __r
     const float4 sc = load_scale4<kScaleBf16>(S0, (long)e * N + c);
     v = f32x4{v[0] * sc.x, v[1] * sc.y, v[2] * sc.z, v[3] * sc.w};
   }
-  *reinterpret_cast<f32x4*>(y_rows + o) = v;
+  if constexpr (kOut == 0) {
+    *reinterpret_cast<f32x4*>(static_cast<float*>(out) + o) = v;
+  } else {
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc[q] += 1.0f * v[q];
+    if constexpr (kOut == 1) {
+      bf16x4 b;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) b[q] = (__bf16)acc[q];
+      *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(out) + o) = b;
+    } else {
+      *reinterpret_cast<f32x4*>(static_cast<float*>(out) + o) = acc;
+    }
+  }
 }
 
 template <bool kGateUp, typename Act, bool kScaleBf16, int F, int RB, int KS>
@@ -859,35 +886,47 @@ hipError_t launch_stream_shared_gu_w(const FfnArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Workgroup shape of the shared-activation gate/up pass.
+// Workgroup shape of the shared-activation gate/up pass (ng 16-channel groups
+// per item, wi items, reductions cut in ks slices).
 //   - Enough items for two 4-wave workgroups per CU: WI = 4 items, no split.
-//   - Else, with a third of an expert's items giving every CU a workgroup: WI = 3
-//     items with their reductions cut in two (KS = 2), six waves on the four
-//     SIMDs, where three unsplit items would leave one SIMD of every CU idle
-//     (the dense MLP layer: gate/up 90-96 -> 82-84 us).
+//   - Else, with 48-channel items (f a multiple of 96) of which two per
+//     workgroup give every CU a workgroup: WI = 2 items cut in two (KS = 2),
+//     four waves, one per SIMD (the dense MLP layer: gate/up 82-84 -> 72-73 us,
+//     A/B on one box, where the six-wave shape below leaves two SIMDs with
+//     two waves and two with one, and every step waits for the busier ones).
+//   - Else, with a third of an expert's 32-channel items giving every CU a
+//     workgroup: WI = 3 items with their reductions cut in two, six waves on
+//     the four SIMDs, where three unsplit items would leave one SIMD of every
+//     CU idle (the dense MLP layer: gate/up 90-96 -> 82-84 us).
 //   - Else the most of 4, 3, 2 items that divides an expert's items and still
 //     gives every CU a workgroup; 2 always divides (f is a multiple of 64).
+// The split shapes need an even number of 64-wide reduction steps and weights
+// of one piece per step (int8, fp8); bf16 weights, whose ring of two-piece
+// steps does not fit two waves per SIMD, take the three items unsplit.
 struct SharedGuShape {
-  int wi, ks;
+  int ng, wi, ks;
 };
-SharedGuShape shared_gu_shape(int E, int f, int d) {
+SharedGuShape shared_gu_shape(int E, int f, int d, bool one_piece) {
   const int gpe = f / (16 * MOE_STREAM_NG_GU_WIDE);
   const long cus = MOE_STREAM_SHARED_MIN_WGS;
-  if (gpe % 4 == 0 && (long)E * (gpe / 4) >= 2 * cus) return {4, 1};
-  if (gpe % 3 == 0 && (long)E * (gpe / 3) >= cus && ((d >> 6) % 2) == 0) return {3, 2};
+  const bool even = ((d >> 6) % 2) == 0;
+  if (gpe % 4 == 0 && (long)E * (gpe / 4) >= 2 * cus) return {MOE_STREAM_NG_GU_WIDE, 4, 1};
+  if (one_piece && even && f % 96 == 0 && (long)E * (f / 96) >= cus) return {3, 2, 2};
+  if (even && gpe % 3 == 0 && (long)E * (gpe / 3) >= cus) return {MOE_STREAM_NG_GU_WIDE, 3, one_piece ? 2 : 1};
   for (int w = 4; w >= 2; --w)
-    if (gpe % w == 0 && (long)E * (gpe / w) >= cus) return {w, 1};
-  return {2, 1};
+    if (gpe % w == 0 && (long)E * (gpe / w) >= cus) return {MOE_STREAM_NG_GU_WIDE, w, 1};
+  return {MOE_STREAM_NG_GU_WIDE, 2, 1};
 }
 
 template <bool kScaleBf16, int F>
 hipError_t launch_stream_shared_gu(const FfnArgs& a, hipStream_t stream) {
   constexpr int NG = MOE_STREAM_NG_GU_WIDE;
-  SharedGuShape sh = shared_gu_shape(a.E, a.f, a.d);
-  if constexpr (WFormat<F>::kPieces == 1) {
+  constexpr bool kOnePiece = WFormat<F>::kPieces == 1;
+  const SharedGuShape sh = shared_gu_shape(a.E, a.f, a.d, kOnePiece);
+  if constexpr (kOnePiece) {
+    if (sh.ks == 2 && sh.ng == 3)
+      return launch_stream_shared_gu_w<kScaleBf16, F, 3, 2, 2, MOE_STREAM_P_SHARED_SPLIT>(a, stream);
     if (sh.ks == 2) return launch_stream_shared_gu_w<kScaleBf16, F, NG, 3, 2, MOE_STREAM_P_SHARED_SPLIT>(a, stream);
-  } else if (sh.ks == 2) {
-    sh = {3, 1};   // bf16 weights: a split's ring of two-piece steps does not fit two waves per SIMD
   }
   switch (sh.wi) {
     case 4: return launch_stream_shared_gu_w<kScaleBf16, F, NG, 4, 1, MOE_STREAM_P_SHARED>(a, stream);
@@ -900,39 +939,46 @@ hipError_t launch_stream_shared_gu(const FfnArgs& a, hipStream_t stream) {
 // workgroups needs ([planes, S, d] fp32), or 0 when it is not taken: fewer
 // than 33 rows per expert on average, no split, a slice without a step, h
 // offsets past 32 bits, or channel groups of an expert that do not fill
-// whole workgroups.
+// whole workgroups. The split is the one the in-workgroup split of the
+// 64-row down pass takes (from its item count), so the two agree bit for bit.
 int shared_down_planes(long S, int d, int f, int E) {
-  constexpr int NG = MOE_STREAM_NG_DN_WIDE, W = MOE_STREAM_SHARED_DN_WAVES;
+  constexpr int NG = MOE_STREAM_NG_SHARED_DN, W = MOE_STREAM_SHARED_DN_WAVES;
   if (!MOE_STREAM_SHARED_DN || S <= 32L * E) return 0;
   if ((uint64_t)S * f * 2 >= (1ull << 32)) return 0;
-  const int gpe = d / (16 * NG);
-  if (gpe % W) return 0;
-  const int ks = choose_split((long)E * gpe, 4);
+  if ((d / (16 * NG)) % W || d % (16 * NG)) return 0;
+  const int ks = choose_split((long)E * (d / (16 * MOE_STREAM_NG_DN_WIDE)), 4);
   if (ks <= 1 || (f >> 6) < ks) return 0;
   return ks;
 }
 
+template <int F, int kOut>
+hipError_t launch_split_down_reduce(const FfnArgs& a, int KS, void* out, hipStream_t stream) {
+  const dim3 rgrid((unsigned)a.S, (unsigned)((a.d + 1023) / 1024));
+  if (!WFormat<F>::kScaled) {
+    hipLaunchKernelGGL((split_down_reduce_kernel<true, false, kOut>), rgrid, dim3(256), 0, stream, a.part, KS, a.S,
+                       a.d, a.offsets, a.E, a.s_down, out);
+  } else if (a.scale_bf16) {
+    hipLaunchKernelGGL((split_down_reduce_kernel<true, true, kOut>), rgrid, dim3(256), 0, stream, a.part, KS, a.S,
+                       a.d, a.offsets, a.E, a.s_down, out);
+  } else {
+    hipLaunchKernelGGL((split_down_reduce_kernel<false, true, kOut>), rgrid, dim3(256), 0, stream, a.part, KS, a.S,
+                       a.d, a.offsets, a.E, a.s_down, out);
+  }
+  return hipGetLastError();
+}
+
 template <int F>
 hipError_t launch_stream_shared_dn(const FfnArgs& a, int KS, hipStream_t stream) {
-  constexpr int NG = MOE_STREAM_NG_DN_WIDE, W = MOE_STREAM_SHARED_DN_WAVES;
+  constexpr int NG = MOE_STREAM_NG_SHARED_DN, W = MOE_STREAM_SHARED_DN_WAVES;
   const int gpe = a.d / (16 * NG);
   const dim3 grid((unsigned)((long)a.E * (gpe / W) * KS));
   hipLaunchKernelGGL((ffn_stream_shared_dn_kernel<F, NG, W, MOE_STREAM_P_SHARED_DN>), grid, dim3(W * kWave), 0,
                      stream, static_cast<const __bf16*>(a.h), a.w_down, a.offsets, a.E, a.d, a.f, a.S, KS, a.part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const dim3 rgrid((unsigned)a.S, (unsigned)((a.d + 1023) / 1024));
-  if (!WFormat<F>::kScaled) {
-    hipLaunchKernelGGL((split_down_reduce_kernel<true, false>), rgrid, dim3(256), 0, stream, a.part, KS, a.S, a.d,
-                       a.offsets, a.E, a.s_down, a.y_rows);
-  } else if (a.scale_bf16) {
-    hipLaunchKernelGGL((split_down_reduce_kernel<true, true>), rgrid, dim3(256), 0, stream, a.part, KS, a.S, a.d,
-                       a.offsets, a.E, a.s_down, a.y_rows);
-  } else {
-    hipLaunchKernelGGL((split_down_reduce_kernel<false, true>), rgrid, dim3(256), 0, stream, a.part, KS, a.S, a.d,
-                       a.offsets, a.E, a.s_down, a.y_rows);
-  }
-  return hipGetLastError();
+  if (!a.y_dense) return launch_split_down_reduce<F, 0>(a, KS, a.y_rows, stream);
+  return a.act_bf16 ? launch_split_down_reduce<F, 1>(a, KS, a.y_dense, stream)
+                    : launch_split_down_reduce<F, 2>(a, KS, a.y_dense, stream);
 }
 
 // Rows per pass: 16*RB. More than 32 rows per expert on average (a dense MLP
@@ -944,6 +990,7 @@ hipError_t launch_stream_shared_dn(const FfnArgs& a, int KS, hipStream_t stream)
 template <bool kGateUp, typename Act, bool kScaleBf16, int F>
 hipError_t launch_stream_pass(const FfnArgs& a, hipStream_t stream) {
   if (a.ids && !(kGateUp && stream_gate_up_takes_ids(a.S, a.E))) return hipErrorInvalidValue;
+  if (!kGateUp && a.y_dense && (a.E != 1 || a.K != 1 || (long)a.S <= 32L * a.E)) return hipErrorInvalidValue;
   if ((long)a.S > 32L * a.E) {
     if constexpr (kGateUp && sizeof(Act) == 2) {
       if (MOE_STREAM_SHARED_GU && (uint64_t)a.T * a.d * 2 < (1ull << 32))
@@ -952,6 +999,7 @@ hipError_t launch_stream_pass(const FfnArgs& a, hipStream_t stream) {
     if constexpr (!kGateUp) {
       const int planes = shared_down_planes(a.S, a.d, a.f, a.E);
       if (a.part && planes > 0) return launch_stream_shared_dn<F>(a, planes, stream);
+      if (a.y_dense) return hipErrorInvalidValue;
     }
     return launch_stream_pass_rb<kGateUp, Act, kScaleBf16, F, 4>(a, stream);
   }

@@ -31,6 +31,11 @@ struct FfnArgs {
   __bf16* h;                  // [S, f] scratch
   float* y_rows;              // [S, d] out
   float* part;                // [planes, S, d] scratch of a down pass split over workgroups, or null
+  // A dense layer (E = K = 1, every token its own row with weight 1) whose
+  // down pass splits its reduction over workgroups: the sum of the slices goes
+  // straight to y ([T, d], act dtype), as the combine would write it, and
+  // y_rows is not written. Null otherwise.
+  void* y_dense;
   // gate/up from the expert ids (S <= 256, 32-row stream pass): ids [S] in,
   // the permutation (offsets, sorted_slots, slot_to_row) out; null otherwise
   const int32_t* ids;

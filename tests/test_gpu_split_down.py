@@ -52,8 +52,12 @@ def _base_workspace(T, d, f, E, K):
 
 
 @pytest.mark.parametrize("fmt,act", [("int8", "bf16"), ("bf16", "bf16"), ("fp8", "bf16"), ("int8", "f32")])
-@pytest.mark.parametrize("T,d,f,E,K", [(300, 256, 512, 16, 2), (100, 512, 640, 4, 2), (150, 256, 1024, 2, 2)])
+@pytest.mark.parametrize("T,d,f,E,K", [(300, 256, 512, 16, 2), (100, 512, 640, 4, 2), (150, 256, 1024, 2, 2),
+                                       (64, 256, 24576, 1, 1), (400, 256, 1536, 16, 2)])
 def test_fused_split_equals_staged_and_oracle(fmt, act, T, d, f, E, K):
+    """The last two shapes take the one-wave-per-SIMD gate/up shape (48-channel
+    items, two per workgroup, reductions cut in two) with int8 and fp8 weights:
+    a dense layer with 256 workgroups, and 16 experts with 16 each."""
     w = workloads.Workload("split", T=T, d=d, f=f, E=E, K=K, act=act, scale=act, weight_src="f32" if act == "f32" else "bf16",
                            seed=21)
     x = workloads.draw_activations(w)
@@ -84,13 +88,17 @@ def test_fused_split_equals_staged_and_oracle(fmt, act, T, d, f, E, K):
 
 
 @pytest.mark.parametrize("path", [MOE_PATH_STREAM, MOE_PATH_AUTO])
-@pytest.mark.parametrize("T", [40, 64])
-def test_dense_mlp_split_equals_staged(path, T):
-    w = workloads.Workload("dsplit", T=T, d=256, f=1024, E=1, K=1, act="bf16", scale="bf16", weight_src="bf16",
-                           seed=8)
+@pytest.mark.parametrize("T,act", [(40, "bf16"), (64, "bf16"), (48, "f32")])
+def test_dense_mlp_split_equals_staged(path, T, act):
+    """moe_mlp_forward with the down reduction split over workgroups writes y
+    from the sum of the slices (the combine folded in): bitwise the staged
+    calls' y, for bf16 and fp32 outputs."""
+    w = workloads.Workload("dsplit", T=T, d=256, f=1024, E=1, K=1, act=act, scale=act,
+                           weight_src="f32" if act == "f32" else "bf16", seed=8)
     x = workloads.draw_activations(w)
     ex, W = _experts("int8", w)
-    assert workspace_size(make_shape(T, 256, 1024, 1, 1, torch.bfloat16, torch.bfloat16, path, MOE_W_INT8)) > \
+    adt = workloads.TORCH_DTYPE[act]
+    assert workspace_size(make_shape(T, 256, 1024, 1, 1, adt, adt, path, MOE_W_INT8)) > \
         _base_workspace(T, 256, 1024, 1, 1)
     xg = x.cuda()
     y = moe_mlp_forward(xg, ex, path=path)
@@ -98,11 +106,12 @@ def test_dense_mlp_split_equals_staged(path, T):
     off = torch.tensor([0, T], dtype=torch.int32, device="cuda")
     ident = torch.arange(T, dtype=torch.int32, device="cuda")
     rows = moe_expert_ffn(xg, off, ident, ex, 1, path=MOE_PATH_STREAM)
-    y2 = moe_combine(rows, ident, ones, torch.bfloat16)
+    y2 = moe_combine(rows, ident, ones, adt)
     h = moe_expert_gate_up(xg, off, ident, ex, 1, path=MOE_PATH_STREAM)
-    r_in = moe_expert_down(h, off, ex, T, 1, path=MOE_PATH_STREAM, split_workspace=False)
+    r_in = moe_expert_down(h, off, ex, T, 1, act=adt, path=MOE_PATH_STREAM, split_workspace=False)
     torch.cuda.synchronize()
-    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+    bits = torch.int16 if act == "bf16" else torch.int32
+    assert torch.equal(y.view(bits), y2.view(bits))
     assert torch.equal(r_in, rows)
     ref = omoe.expert_swiglu(np64(x), W["q_gate"][0], W["s_gate"][0], W["q_up"][0], W["s_up"][0],
                              W["q_down"][0], W["s_down"][0])
