@@ -4,7 +4,9 @@
 A step is one forward of the whole layer (router + top-K gate, permutation,
 gate/up contraction with SwiGLU, down contraction, weighted combine) over one
 batch of synthetic tokens, through the fused C-ABI call moe_forward. Inputs
-and int8 weights are resident in HBM before timing starts.
+and int8 weights are resident in HBM before timing starts. Each timed region
+of K steps follows W warm-up steps, and before those the step runs untimed
+for at least PREWARM_MS (the clocks ramp up over tens of milliseconds).
 
 Default (headline) workload: the Jamba-1.5-Large-shaped MoE layer at prefill
 with skewed routing, T=16384 tokens, d=8192, f=24576, 16 experts, top-2,
@@ -124,6 +126,23 @@ def ffn_path_used(w, path):
 
 
 # ----------------------------------------------------------------------------- timing
+# Untimed run of the step itself before its warm-up steps, at least this long:
+# the GPU's clocks take tens of milliseconds to ramp up from a lighter load,
+# which a few warm-up steps of a sub-millisecond decode step do not cover
+# (the Large dense MLP at T=64 measured 157, 154, then 140 us per step over
+# three back-to-back 20-step regions after 5 warm-up steps, 132 us after 200).
+PREWARM_MS = 200.0
+
+
+def prewarm(step):
+    import torch
+    t_end = time.perf_counter() + PREWARM_MS * 1e-3
+    while time.perf_counter() < t_end:
+        for _ in range(8):
+            step()
+        torch.cuda.synchronize()
+
+
 def time_forward(layer, x, path, steps, warmup, dense=False):
     """Step time of the fused call: moe_forward, or moe_mlp_forward for a dense MLP layer.
 
@@ -156,6 +175,7 @@ def time_forward(layer, x, path, steps, warmup, dense=False):
         if st:
             _lib.check(st)
 
+    prewarm(step)
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -245,6 +265,7 @@ def time_stages(layer, x, path, steps, warmup, dense=False):
 
     n_ev = len(names) + 1
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(steps)]
+    prewarm(lambda: step([torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]))
     for _ in range(warmup):
         step([torch.cuda.Event(enable_timing=True) for _ in range(n_ev)])
     torch.cuda.synchronize()
@@ -482,6 +503,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "prewarm_ms": PREWARM_MS,
         "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
