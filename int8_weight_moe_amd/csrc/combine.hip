@@ -1,8 +1,11 @@
 // Weighted combine back to token order: y[t] = sum_k w[t,k] * y_rows[row(t,k)],
 // k ascending, fp32 accumulation, one write per output element (no atomics,
 // so the result is deterministic). Bound by HBM: K fp32 rows in, one row out.
-// Workgroup (t, c): token t, columns 1024*c .. +1024, four per thread, so a
-// decode batch of a few tokens still spreads over many workgroups.
+// Workgroup (t, c): token t, columns 2048*c .. +2048, eight per thread, so a
+// decode batch of a few tokens still spreads over many workgroups. y_rows is
+// read once: non-temporal loads. Measured against four columns per thread
+// with ordinary loads (interleaved repetitions on one box): Large prefill
+// (16384 tokens, d = 8192) 280 -> 248 us, Mini prefill 66.6 -> 61.2 us.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -11,7 +14,13 @@ namespace moe {
 namespace {
 
 constexpr int kCombineThreads = 256;
-constexpr int kCombineCols = kCombineThreads * 4;
+constexpr int kVec = 8;   // columns per thread (d is a multiple of 64)
+constexpr int kCombineCols = kCombineThreads * kVec;
+
+__device__ __forceinline__ float4 load_nt_f4(const float* p) {
+  const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+  return make_float4(v[0], v[1], v[2], v[3]);
+}
 
 template <bool kOutBf16>
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float* __restrict__ y_rows,
@@ -19,32 +28,42 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float* _
                                                                   const float* __restrict__ topk_w, int T, int d,
                                                                   int K, void* __restrict__ y) {
   const int t = blockIdx.x;
-  const int c = blockIdx.y * kCombineCols + threadIdx.x * 4;
+  const int c = blockIdx.y * kCombineCols + threadIdx.x * kVec;
   if (c >= d) return;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  float4 acc[kVec / 4];
+#pragma unroll
+  for (int v = 0; v < kVec / 4; ++v) acc[v] = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     if (k < K) {
       const int row = slot_to_row[(long)t * K + k];
       const float w = topk_w[(long)t * K + k];
       if (row >= 0) {
-        const float4 v = *reinterpret_cast<const float4*>(y_rows + (long)row * d + c);
-        acc.x += w * v.x;
-        acc.y += w * v.y;
-        acc.z += w * v.z;
-        acc.w += w * v.w;
+        float4 vv[kVec / 4];
+#pragma unroll
+        for (int v = 0; v < kVec / 4; ++v) vv[v] = load_nt_f4(y_rows + (long)row * d + c + 4 * v);
+#pragma unroll
+        for (int v = 0; v < kVec / 4; ++v) {
+          acc[v].x += w * vv[v].x;
+          acc[v].y += w * vv[v].y;
+          acc[v].z += w * vv[v].z;
+          acc[v].w += w * vv[v].w;
+        }
       }
     }
   }
-  if constexpr (kOutBf16) {
-    bf16x4 o;
-    o[0] = (__bf16)acc.x;
-    o[1] = (__bf16)acc.y;
-    o[2] = (__bf16)acc.z;
-    o[3] = (__bf16)acc.w;
-    *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(y) + (long)t * d + c) = o;
-  } else {
-    *reinterpret_cast<float4*>(static_cast<float*>(y) + (long)t * d + c) = acc;
+#pragma unroll
+  for (int v = 0; v < kVec / 4; ++v) {
+    if constexpr (kOutBf16) {
+      bf16x4 o;
+      o[0] = (__bf16)acc[v].x;
+      o[1] = (__bf16)acc[v].y;
+      o[2] = (__bf16)acc[v].z;
+      o[3] = (__bf16)acc[v].w;
+      *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(y) + (long)t * d + c + 4 * v) = o;
+    } else {
+      *reinterpret_cast<float4*>(static_cast<float*>(y) + (long)t * d + c + 4 * v) = acc[v];
+    }
   }
 }
 
