@@ -58,6 +58,12 @@
  *     A failed check returns MOE_ERR_CHECK (moe_forward: before the down
  *     pass). The checks copy the arrays to the host and synchronise `stream`:
  *     they are for debugging, not for timed runs or graph capture.
+ *   - Logging: while the environment variable MOE_LOG is set (to a value
+ *     other than "0"), every call that runs an expert-FFN pass writes one line
+ *     per pass to stderr ("[moe] <call> gate/up|down: <shape>; <schedule>"):
+ *     the schedule (stream or tiled), and for the stream schedule the rows per
+ *     pass, where the expert segments come from, and whether the down pass
+ *     splits its reduction over workgroups. Nothing else changes.
  */
 #ifndef MOE_INT8_H
 #define MOE_INT8_H

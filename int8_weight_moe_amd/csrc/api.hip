@@ -221,13 +221,49 @@ moe::FfnArgs ffn_args(const moe_shape* s, const void* x, const int32_t* offsets,
   return a;
 }
 
-moe_status run_gate_up(const moe_shape* s, const moe::FfnArgs& a, hipStream_t stream) {
+// ---- MOE_LOG: one line per FFN pass on stderr, naming the schedule it takes
+
+// Set and not "0" at the time of the call.
+bool log_on() {
+  const char* v = getenv("MOE_LOG");
+  return v && v[0] && strcmp(v, "0") != 0;
+}
+
+void log_pass(const char* call, bool gate_up, const moe_shape* s, const moe::FfnArgs& a) {
+  const long S = (long)s->T * s->K;
+  char how[192];
+  if (!use_stream(s)) {
+    snprintf(how, sizeof(how), "tiled schedule, %s",
+             (gate_up ? a.claims_gate_up : a.claims_down) ? "the last tiles of each XCD queue claimed"
+                                                          : "static tile order");
+  } else if (gate_up) {
+    snprintf(how, sizeof(how), "stream schedule, %d-row passes, expert segments %s", S > 32L * s->E ? 64 : 32,
+             a.ids ? "derived from the expert ids (permutation written by the pass)" : "read from the permutation");
+  } else {
+    const int planes = moe::stream_down_planes(S, s->d, s->f, s->E);
+    if (a.part && planes > 0) {
+      snprintf(how, sizeof(how), "stream schedule, reduction split over workgroups in %d slices%s", planes,
+               a.y_dense ? ", their sum written to y (combine folded in)" : "");
+    } else {
+      snprintf(how, sizeof(how), "stream schedule, %d-row passes, reduction inside the workgroup",
+               S > 32L * s->E ? 64 : 32);
+    }
+  }
+  static const char* const kFmt[] = {"int8", "bf16", "fp8"};
+  fprintf(stderr, "[moe] %s %s: T=%d d=%d f=%d E=%d K=%d act=%s scale=%s weights=%s; %s\n", call,
+          gate_up ? "gate/up" : "down", s->T, s->d, s->f, s->E, s->K, s->act_dtype == MOE_BF16 ? "bf16" : "f32",
+          s->scale_dtype == MOE_BF16 ? "bf16" : "f32", kFmt[s->weight_fmt], how);
+}
+
+moe_status run_gate_up(const char* call, const moe_shape* s, const moe::FfnArgs& a, hipStream_t stream) {
+  if (log_on()) log_pass(call, true, s, a);
   const hipError_t e = use_stream(s) ? moe::launch_stream_gate_up(a, stream) : moe::launch_tiled_gate_up(a, stream);
   if (e != hipSuccess) return hip_fail(e, "gate/up launch");
   return MOE_OK;
 }
 
-moe_status run_down(const moe_shape* s, const moe::FfnArgs& a, hipStream_t stream) {
+moe_status run_down(const char* call, const moe_shape* s, const moe::FfnArgs& a, hipStream_t stream) {
+  if (log_on()) log_pass(call, false, s, a);
   const hipError_t e = use_stream(s) ? moe::launch_stream_down(a, stream) : moe::launch_tiled_down(a, stream);
   if (e != hipSuccess) return hip_fail(e, "down launch");
   return MOE_OK;
@@ -279,10 +315,10 @@ moe_status scratch_on_current_device(void** out) {
   return MOE_OK;
 }
 
-moe_status forward_impl(const moe_shape* s, const void* x, const void* router_w, const float* router_bias,
-                       const void* w_gate, const void* w_up, const void* w_down, const void* s_gate,
-                       const void* s_up, const void* s_down, void* y, int32_t* topk_ids_out, float* topk_w_out,
-                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
+moe_status forward_impl(const char* call, const moe_shape* s, const void* x, const void* router_w,
+                       const float* router_bias, const void* w_gate, const void* w_up, const void* w_down,
+                       const void* s_gate, const void* s_up, const void* s_down, void* y, int32_t* topk_ids_out,
+                       float* topk_w_out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   moe_status st = check_shape(s);
   if (st != MOE_OK) return st;
   st = check_ffn(s);
@@ -330,7 +366,7 @@ moe_status forward_impl(const moe_shape* s, const void* x, const void* router_w,
     a.perm_offsets = offsets;
     a.perm_sorted = sorted;
     a.perm_s2r = s2r;
-    st = run_gate_up(s, a, stream);
+    st = run_gate_up(call, s, a, stream);
     a.ids = nullptr;
     if (st == MOE_OK && debug_on()) st = debug_permutation(s, ids, offsets, sorted, s2r, stream);
   } else {
@@ -340,10 +376,10 @@ moe_status forward_impl(const moe_shape* s, const void* x, const void* router_w,
       st = debug_permutation(s, ids, offsets, sorted, s2r, stream);
       if (st != MOE_OK) return st;
     }
-    st = run_gate_up(s, a, stream);
+    st = run_gate_up(call, s, a, stream);
   }
   if (st != MOE_OK) return st;
-  st = run_down(s, a, stream);
+  st = run_down(call, s, a, stream);
   if (st != MOE_OK) return st;
   e = moe::launch_combine(y_rows, s2r, wts, s->T, s->d, s->K, s->act_dtype == MOE_BF16, y, stream);
   if (e != hipSuccess) return hip_fail(e, "combine launch");
@@ -454,9 +490,9 @@ moe_status moe_expert_ffn(const moe_shape* s, const void* x, const int32_t* expe
     a.claims_down = reinterpret_cast<unsigned long long*>(dws);
     a.claims_gate_up = reinterpret_cast<unsigned long long*>(dws + round_up(down_ws_bytes(s)));
   }
-  st = run_gate_up(s, a, stream);
+  st = run_gate_up("moe_expert_ffn", s, a, stream);
   if (st != MOE_OK) return st;
-  return run_down(s, a, stream);
+  return run_down("moe_expert_ffn", s, a, stream);
 }
 
 moe_status moe_expert_gate_up(const moe_shape* s, const void* x, const int32_t* expert_offsets,
@@ -486,7 +522,7 @@ moe_status moe_expert_gate_up(const moe_shape* s, const void* x, const int32_t* 
   moe::FfnArgs a = ffn_args(s, x, expert_offsets, sorted_slots, w_gate, w_up, nullptr, s_gate, s_up, nullptr,
                             nullptr, static_cast<__bf16*>(h));
   if (workspace && need) a.claims_gate_up = static_cast<unsigned long long*>(workspace);
-  return run_gate_up(s, a, stream);
+  return run_gate_up("moe_expert_gate_up", s, a, stream);
 }
 
 moe_status moe_expert_down(const moe_shape* s, const void* h, const int32_t* expert_offsets, const void* w_down,
@@ -518,7 +554,7 @@ moe_status moe_expert_down(const moe_shape* s, const void* h, const int32_t* exp
       a.claims_down = static_cast<unsigned long long*>(workspace);
     }
   }
-  return run_down(s, a, stream);
+  return run_down("moe_expert_down", s, a, stream);
 }
 
 moe_status moe_down_workspace_size(const moe_shape* shape, size_t* bytes) {
@@ -557,8 +593,8 @@ moe_status moe_forward(const moe_shape* s, const void* x, const void* router_w, 
                        const void* w_gate, const void* w_up, const void* w_down, const void* s_gate,
                        const void* s_up, const void* s_down, void* y, int32_t* topk_ids_out, float* topk_w_out,
                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  return forward_impl(s, x, router_w, router_bias, w_gate, w_up, w_down, s_gate, s_up, s_down, y, topk_ids_out,
-                      topk_w_out, workspace, workspace_bytes, stream);
+  return forward_impl("moe_forward", s, x, router_w, router_bias, w_gate, w_up, w_down, s_gate, s_up, s_down, y,
+                      topk_ids_out, topk_w_out, workspace, workspace_bytes, stream);
 }
 
 moe_status moe_forward_noalloc(const moe_shape* s, const void* x, const void* router_w, const float* router_bias,
@@ -575,8 +611,8 @@ moe_status moe_forward_noalloc(const moe_shape* s, const void* x, const void* ro
   void* ws = nullptr;
   st = scratch_on_current_device(&ws);
   if (st != MOE_OK) return st;
-  return forward_impl(s, x, router_w, router_bias, w_gate, w_up, w_down, s_gate, s_up, s_down, y, topk_ids_out,
-                      topk_w_out, ws, kScratchBytes, stream);
+  return forward_impl("moe_forward_noalloc", s, x, router_w, router_bias, w_gate, w_up, w_down, s_gate, s_up,
+                      s_down, y, topk_ids_out, topk_w_out, ws, kScratchBytes, stream);
 }
 
 moe_status moe_mlp_workspace_size(const moe_shape* shape, size_t* bytes) {
@@ -627,9 +663,9 @@ moe_status moe_mlp_forward(const moe_shape* s, const void* x, const void* w_gate
   // with the down pass's reduction split over workgroups, the sum of its slices
   // is written to y directly (the combine of one expert of weight 1)
   if (L.part_bytes) a.y_dense = y;
-  st = run_gate_up(s, a, stream);
+  st = run_gate_up("moe_mlp_forward", s, a, stream);
   if (st != MOE_OK) return st;
-  st = run_down(s, a, stream);
+  st = run_down("moe_mlp_forward", s, a, stream);
   if (st != MOE_OK || a.y_dense) return st;
   e = moe::launch_combine(y_rows, s2r, wts, s->T, s->d, 1, s->act_dtype == MOE_BF16, y, stream);
   if (e != hipSuccess) return hip_fail(e, "combine launch");

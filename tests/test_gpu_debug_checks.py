@@ -1,4 +1,5 @@
-"""MOE_DEBUG: the C ABI's host-side permutation checks, through the library.
+"""MOE_DEBUG: the C ABI's host-side permutation checks, through the library
+(and MOE_LOG, the line per FFN pass naming the schedule taken).
 
 With MOE_DEBUG set, the calls that take a permutation from the caller check it
 before anything is launched, and the calls that produce one check it after it
@@ -14,7 +15,7 @@ import torch
 
 import workloads
 from int8_weight_moe_amd import (MoeError, moe_combine, moe_expert_down, moe_expert_ffn, moe_expert_gate_up,
-                                 moe_forward, moe_permute)
+                                 moe_forward, moe_forward_noalloc, moe_mlp_forward, moe_permute)
 from int8_weight_moe_amd._lib import MOE_PATH_AUTO, MOE_PATH_STREAM, MOE_PATH_TILED
 from oracle import moe as omoe
 from tests.helpers import experts_to_device, quantize_experts_oracle
@@ -145,3 +146,37 @@ def test_bad_caller_permutations_are_rejected_before_launch(monkeypatch):
     moe_expert_gate_up(xg, dev(off), dev(ss), ex, K, h=h_big[:S])
     torch.cuda.synchronize()
     assert not torch.equal(h_big[:S], h_ref[:S]) and torch.equal(h_big[S:], h_ref[S:])
+
+
+def test_moe_log_names_the_schedule(monkeypatch, capfd):
+    """With MOE_LOG set, one stderr line per FFN pass names the schedule: the
+    stream passes of a decode batch (segments from the ids), of a larger batch
+    (segments from the permutation), the tiled passes with claimed tails, and a
+    dense layer whose down reduction is split with the combine folded in.
+    Unset, the library writes nothing."""
+    d, f, E, K = 256, 512, 16, 2
+    monkeypatch.delenv("MOE_LOG", raising=False)
+    x, wr, ex = _layer(600, d, f, E, K)
+    xg, wrg = x.cuda(), wr.cuda()
+    moe_forward(xg[:8], wrg, None, ex, K)
+    torch.cuda.synchronize()
+    assert "[moe]" not in capfd.readouterr().err
+    monkeypatch.setenv("MOE_LOG", "1")
+    moe_forward(xg[:8], wrg, None, ex, K)
+    moe_forward_noalloc(xg[:200], wrg, None, ex, K, path=MOE_PATH_STREAM)
+    moe_forward(xg, wrg, None, ex, K, path=MOE_PATH_TILED)
+    dx, _, dex = _layer(64, d, 1024, 1, 1, seed=4)
+    moe_mlp_forward(dx.cuda(), dex)
+    torch.cuda.synchronize()
+    lines = [l for l in capfd.readouterr().err.splitlines() if l.startswith("[moe]")]
+    assert len(lines) == 8, lines
+    assert lines[0].startswith("[moe] moe_forward gate/up: T=8 d=256 f=512 E=16 K=2 act=bf16 scale=bf16 weights=int8;")
+    assert "stream schedule, 32-row passes, expert segments derived from the expert ids" in lines[0]
+    assert "moe_forward down:" in lines[1] and "reduction inside the workgroup" in lines[1]
+    assert lines[2].startswith("[moe] moe_forward_noalloc gate/up: T=200")
+    assert "expert segments read from the permutation" in lines[2]
+    assert "tiled schedule, the last tiles of each XCD queue claimed" in lines[4]
+    assert "tiled schedule" in lines[5]
+    assert lines[6].startswith("[moe] moe_mlp_forward gate/up: T=64 d=256 f=1024 E=1 K=1")
+    assert "64-row passes" in lines[6]
+    assert "reduction split over workgroups in 8 slices, their sum written to y" in lines[7]
