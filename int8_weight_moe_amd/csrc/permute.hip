@@ -6,9 +6,10 @@
 // the MoE layer is I/O-bound).
 //
 // Fewer than 4 chunks of 2048 slots (decode, small batches): one workgroup of
-// 16 waves. Wave w owns a contiguous range of slots, walked in 64-slot chunks (the ids of 8 chunks loaded together). Pass 1 counts, per
-// chunk and expert, the lanes whose id matches (a ballot and a popcount),
-// accumulated by the lane that owns that expert. The 16 x E counts are scanned
+// 16 waves. Wave w owns a contiguous range of slots, walked in 64-slot chunks
+// (the ids of 8 chunks loaded together). Pass 1 counts, per chunk and expert,
+// the lanes whose id matches (a ballot and a popcount), accumulated by the
+// lane that owns that expert. The 16 x E counts are scanned
 // in a fixed order (expert-major, then wave) by the whole workgroup, one count
 // per thread. Pass 2 walks the same chunks again and gives each slot its
 // position: the expert's running base plus the number of matching lanes below
